@@ -1,0 +1,36 @@
+"""CPU oracle for SageAttention2-style quantized attention (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP kernels behind
+the C ABI and their Python binding) never calls it and shares no code with it.
+
+Two parts, each citing the passage of the pages it follows:
+
+* ``attention.exact_attention`` -- textbook softmax attention in float64 on the
+  exactly promoted fp16/bf16 inputs (the full-precision output O that the
+  SageAttention2++ summary, "A.2 Datasets and Metrics", compares O' against).
+* ``quant`` + ``attention.emulate_attention`` -- the quantisation pipeline of the
+  SageAttention2 abstract and the SageAttention2++ summary ("2.1
+  SageAttention2"): Q, K smoothing and INT8 / INT4-range quantisation with
+  per-group scales, P~ and V to FP8 E4M3, and the FlashAttention-style tiled
+  online softmax ("2. Preliminary").  Codes, scales and means follow fp32
+  arithmetic exactly; the attention output is float64 apart from the fp32
+  values that decide an FP8 code.
+* ``metrics`` -- cosine similarity, relative L1 and RMSE ("A.2").
+* ``fp8`` -- the OCP E4M3 ("fn") format, decoded from its definition and
+  encoded by nearest-value search with ties to the even code.
+
+Pins (tests that tie each function to something other than itself) live in
+``tests/test_oracle_*.py``.  One reading has no pin from the pages: the pages
+print no worked values for the quantized output, so agreement of this
+emulation with the papers' own kernels is "parity unpinned"; what is pinned is
+agreement with exact attention when quantisation is switched off, the
+quantiser invariants, the codec, and the reduction order.
+"""
+from . import fp8, reduce, quant, attention, metrics  # noqa: F401
+
+from .fp8 import e4m3_decode, e4m3_encode  # noqa: F401
+from .reduce import canonical_sum, canonical_mean, pad_length  # noqa: F401
+from .quant import QuantParams, quant_qk, quant_v, q_group_index, k_group_index  # noqa: F401
+from .attention import exact_attention, exact_attention_rows, emulate_attention, emulate_block  # noqa: F401
+from .metrics import cosine, rel_l1, rmse, compare  # noqa: F401

@@ -1,0 +1,165 @@
+"""Attention: exact float64 reference and the tiled quantized emulation.
+
+exact_attention: O = softmax(sm_scale * Q K^T + M) V in float64 on the exactly
+promoted inputs; M is -inf where key j > query i when causal (square,
+top-left aligned).  This is the full-precision O of the SageAttention2++
+summary, "A.2 Datasets and Metrics".
+
+emulate_attention: the FlashAttention-style tiled online softmax the
+SageAttention2++ summary describes in "2. Preliminary" and "2.1 SageAttention2",
+on the codes produced by ``oracle.quant``:
+
+    for each 128-query block, key tiles of BK keys in ascending order
+    (tiles wholly above the diagonal are skipped when causal):
+      s   = (S_int * dQ_i * dK_j + dS_j) * sm_scale * log2(e)   (fp64 -> fp32)
+      s   = -inf for padded keys (j >= N) and, when causal, for j > i
+      m'  = max(m, max_j s);  alpha = 2^(m - m')  (0 while m = -inf)
+      P~  = 2^(s - m')                                         (fp64 -> fp32)
+      l   = alpha * l + sum_j P~
+      p^  = E4M3(P~ * P_r)        (the fixed per-block scale 1 / P_r)
+      acc = alpha * acc + sum_j dec(p^_j) * dec(v^_j)
+    O = acc * dV / (P_r * l) + mu_V, rounded once to the output dtype.
+
+Everything except the fp32 values that decide an E4M3 code is float64.  The
+max is updated once per tile, so the emulated P~ depends on BK; it is a
+parameter that must equal the kernel's tile (128).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .fp8 import e4m3_decode, e4m3_encode
+from .quant import QBLOCK, q_group_index, k_group_index, bias_row
+
+LOG2E = 1.0 / math.log(2.0)
+DEFAULT_BK = 128
+
+
+def _default_scale(d: int, sm_scale):
+    return 1.0 / math.sqrt(d) if not sm_scale else float(sm_scale)
+
+
+def exact_attention_rows(q, k, v, rows, causal=False, sm_scale=None):
+    """Exact float64 attention for one head and the given query rows.
+
+    q, k, v: [N, d] arrays; rows: 1-D int array of query indices.  Returns
+    [len(rows), d] float64.
+    """
+    q64 = np.asarray(q, np.float64)
+    k64 = np.asarray(k, np.float64)
+    v64 = np.asarray(v, np.float64)
+    N, d = k64.shape
+    scale = _default_scale(d, sm_scale)
+    rows = np.asarray(rows)
+    s = (q64[rows] @ k64.T) * scale
+    if causal:
+        s = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, s)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v64
+
+
+def exact_attention(q, k, v, causal=False, sm_scale=None, row_block=256):
+    """Exact float64 attention over [B,H,N,d] inputs."""
+    B, H, N, d = q.shape
+    out = np.empty((B, H, N, d), np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                out[b, h, r0:r0 + len(rows)] = exact_attention_rows(q[b, h], k[b, h], v[b, h], rows, causal, sm_scale)
+    return out
+
+
+def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_scale=None,
+                  p_range: float = 448.0, bk: int = DEFAULT_BK, quantized: bool = True):
+    """Emulate one 128-query block; returns (O float64 [rows, d], rows).
+
+    ``quantized=False`` switches every quantiser off (identity codecs: the
+    smoothed fp32 values stand for the codes, scales are 1 and P~ is not
+    rounded to FP8); the result must then equal exact attention up to fp32
+    rounding of s and P~, which pins the tiling, the online softmax and the
+    smoothing add-backs.
+    """
+    N, n_pad = qk["N"], qk["n_pad"]
+    d = qk["q_codes"].shape[-1]
+    scale = _default_scale(d, sm_scale) * LOG2E
+    q0 = qb * QBLOCK
+    nrows = min(QBLOCK, N - q0)
+    qi = q0 + np.arange(QBLOCK)
+    if quantized:
+        qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
+        dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
+        kmat = qk["k_codes"][b, h].astype(np.float64)
+        dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
+        vmat = e4m3_decode(vq["v_codes"][b, h])
+        dv = vq["v_scale"][b, h].astype(np.float64)
+        pr = float(np.float32(p_range))
+    else:
+        qmat = qk["q_smoothed"][b, h, q0:q0 + QBLOCK].astype(np.float64)
+        dq = np.ones(QBLOCK)
+        kmat = qk["k_smoothed"][b, h].astype(np.float64)
+        dk = np.ones(n_pad)
+        vmat = vq["v_smoothed"][b, h].astype(np.float64)
+        dv = np.ones(d)
+        pr = 1.0
+    bias = (qk["bias"][b, h, qb] if qk.get("bias") is not None else bias_row(qk, b, h, qb)).astype(np.float64)
+
+    key_end = min(N, q0 + QBLOCK) if causal else N
+    n_tiles = -(-key_end // bk)
+    m = np.full(QBLOCK, -np.inf)
+    l = np.zeros(QBLOCK)
+    acc = np.zeros((QBLOCK, d))
+    for t in range(n_tiles):
+        j = np.arange(t * bk, min((t + 1) * bk, n_pad))
+        S = qmat @ kmat[j].T                                           # exact integers when quantized
+        s = ((S * (dq[:, None] * dk[None, j]) + bias[None, j]) * scale).astype(np.float32)
+        mask = (j[None, :] >= N) | (causal & (j[None, :] > qi[:, None]))
+        s = np.where(mask, np.float32(-np.inf), s)
+        m_new = np.maximum(m, s.max(axis=1).astype(np.float64))
+        alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - np.where(np.isneginf(m_new), 0.0, m_new)))
+        base = np.where(np.isneginf(m_new), 0.0, m_new)
+        P = np.exp2(s.astype(np.float64) - base[:, None]).astype(np.float32)
+        l = alpha * l + P.astype(np.float64).sum(axis=1)
+        if quantized:
+            pw = e4m3_decode(e4m3_encode((P * np.float32(pr)).astype(np.float32)))
+        else:
+            pw = P.astype(np.float64)
+        acc = alpha[:, None] * acc + pw @ vmat[j]
+        m = m_new
+    o = acc * dv[None, :] / (pr * l[:, None]) + vq["v_mean"][b, h].astype(np.float64)[None, :]
+    return o[:nrows], qi[:nrows]
+
+
+def emulate_attention(qk: dict, vq: dict, causal: bool, sm_scale=None, p_range: float = 448.0,
+                      bk: int = DEFAULT_BK, quantized: bool = True, blocks=None):
+    """Emulate the whole tensor (or the (b, h, qb) triples in ``blocks``).
+
+    Returns float64 [B,H,N,d] (rows of blocks not asked for are NaN).
+    """
+    B, H, n_pad, d = qk["q_codes"].shape
+    N = qk["N"]
+    out = np.full((B, H, N, d), np.nan)
+    if blocks is None:
+        blocks = [(b, h, qb) for b in range(B) for h in range(H) for qb in range(n_pad // QBLOCK)]
+    for (b, h, qb) in blocks:
+        o, rows = emulate_block(qk, vq, b, h, qb, causal, sm_scale, p_range, bk, quantized)
+        out[b, h, rows] = o
+    return out
+
+
+def round_output(o: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 outputs once to fp16/bf16 (nearest, ties to even); float32 result."""
+    o = np.asarray(o, np.float64)
+    if dtype == "fp16":
+        return o.astype(np.float16).astype(np.float32)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    bits = np.ascontiguousarray(o).view(np.uint64)
+    keep = np.uint64(45)
+    rnd = (bits >> keep) & np.uint64(1)
+    bits = (bits + (np.uint64(1) << np.uint64(44)) - np.uint64(1) + rnd) & ~((np.uint64(1) << keep) - np.uint64(1))
+    return bits.view(np.float64).astype(np.float32)
