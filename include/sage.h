@@ -1,0 +1,191 @@
+/*
+ * sage.h -- C ABI of a SageAttention2-style quantized attention forward pass
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the method of "SageAttention2 Technical Report: Accurate 4
+ * Bit Attention for Plug-and-play Inference Acceleration", abstract, and of the
+ * SageAttention2++ summary, sections "2. Preliminary" and "2.1 SageAttention2"):
+ *
+ *   K' = K - mean_tokens(K)                       (per channel, per head)
+ *   Q' = Q - mean_block(Q)                        (per channel, per 128-token block qb)
+ *   dS[qb, j] = mean_block(Q)(qb) . K'_j          (restores the Q mean)
+ *   Q', K'  -> integer codes with per-group scales (INT8, or INT4-range [-7,7]
+ *              held in int8 and run on the INT8 matrix cores)
+ *   V'  = V - mean_tokens(V); V' -> FP8 E4M3 with per-channel scales
+ *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles;
+ *   P~  -> FP8 E4M3 with the fixed scale 1/P_r;  O = sum P~ V' / l + mean(V).
+ *
+ * All entry points are plain C with device pointers, sizes and a HIP stream
+ * (passed as void*, a hipStream_t; NULL is the default stream).  The library
+ * never allocates or frees memory: the caller owns every buffer.  Nothing
+ * synchronises; every call only enqueues work on the given stream.
+ *
+ * Error behaviour: every argument is validated on the host before anything is
+ * enqueued.  A call that returns an error has launched nothing and written
+ * nothing.  SAGE_EHIP reports a launch failure (hipGetLastError); device-side
+ * faults surface at the caller's next synchronisation.  sage_last_error()
+ * returns a thread-local message describing the last failure.  No C++
+ * exception crosses this interface.
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_API __attribute__((visibility("default")))
+
+/* Bumped whenever a buffer layout or a group map below changes. */
+#define SAGE_ABI_VERSION 1
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_EINVAL = 1,       /* bad pointer, shape, stride, alignment or size */
+  SAGE_EUNSUPPORTED = 2, /* valid request outside what this build supports */
+  SAGE_EHIP = 3          /* the HIP runtime reported an error */
+} sage_status;
+
+typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
+
+/* Quantisation groups of Q and K (the pages' "per-block", "warp-level" and
+ * "per-thread" granularities; the SageAttention2 abstract and the
+ * SageAttention2++ summary, 2.1).  Token indices are per head.
+ *   SAGE_GRAN_THREAD: Q group = one token; K group = the 16 keys
+ *                     {32s + 8a + 4h + b : a, b in 0..3} for each 32-key block
+ *                     s and h in {0,1}; K scale index = 2s + h.
+ *   SAGE_GRAN_WARP:   Q group = 32 consecutive tokens; K group = 64 keys.
+ *   SAGE_GRAN_BLOCK:  Q group = 128 consecutive tokens; K group = 64 keys. */
+typedef enum { SAGE_GRAN_THREAD = 0, SAGE_GRAN_WARP = 1, SAGE_GRAN_BLOCK = 2 } sage_gran;
+
+/* Shape of Q, K, V ([B, H, N, d], element type dtype).  Strides are in
+ * elements for the B, H and N dimensions; the d dimension is contiguous.
+ * Every stride must be a multiple of 8 and every tensor pointer 16-byte
+ * aligned.  Supported: d in {64, 128}; 1 <= N <= 2^20; B, H >= 1. */
+typedef struct {
+  int64_t B, H, N, d;
+  int32_t dtype;         /* sage_dtype, shared by Q, K, V and O */
+  int32_t reserved;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+} sage_shape;
+
+/* Method settings.  sage_params_default() fills the defaults shown. */
+typedef struct {
+  int32_t qk_bits;   /* 8 (default) or 4 (INT4-range codes, qmax 7)           */
+  int32_t gran;      /* sage_gran, default SAGE_GRAN_THREAD                   */
+  int32_t smooth_q;  /* 1 (default): subtract the 128-token block mean of Q   */
+  int32_t smooth_k;  /* 1 (default): subtract the token mean of K             */
+  int32_t smooth_v;  /* 1 (default): subtract the token mean of V             */
+  float p_range;     /* P_r in (0, 448], default 448: P~ code = E4M3(P~ * P_r) */
+  float v_range;     /* V_r in (0, 448], default 448: V code = E4M3(V' V_r/amax) */
+  float sm_scale;    /* softmax scale; 0 (default) means 1/sqrt(d)            */
+} sage_params;
+
+/* Device buffers written by sage_quant_qk (N_pad = 128 * ceil(N / 128)).
+ *   q_codes  int8  [B, H, N_pad, d]   row-major, rows >= N hold 0
+ *   q_scale  fp32  [B, H, Gq]         Gq = N_pad (THREAD), N_pad/32 (WARP), N_pad/128 (BLOCK)
+ *   q_mean   fp32  [B, H, N_pad/128, d]
+ *   k_codes  int8  [B, H, N_pad, d]
+ *   k_scale  fp32  [B, H, Gk]         Gk = N_pad/16 (THREAD), N_pad/64 (WARP, BLOCK)
+ *   k_mean   fp32  [B, H, d]
+ *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j]; 0 for j >= N
+ *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)   */
+typedef struct {
+  int8_t* q_codes;
+  float* q_scale;
+  float* q_mean;
+  int8_t* k_codes;
+  float* k_scale;
+  float* k_mean;
+  float* bias;
+  float* k_partial;
+} sage_qk_buffers;
+
+/* Device buffers written by sage_quant_v.
+ *   v_codes  uint8 [B, H, d, N_pad]  E4M3 codes, channel-major.  Within every
+ *            64-key group starting at key 64g, byte 32h + t (h in {0,1},
+ *            t in 0..31) holds key 64g + 32(t/16) + 8((t%16)/4) + 4h + t%4.
+ *            Keys >= N hold 0.
+ *   v_scale  fp32  [B, H, d]   amax_c / V_r
+ *   v_mean   fp32  [B, H, d]
+ *   v_partial fp32 [B, H, N_pad/128, 3, d]   scratch (per-block sum, max, min) */
+typedef struct {
+  uint8_t* v_codes;
+  float* v_scale;
+  float* v_mean;
+  float* v_partial;
+} sage_v_buffers;
+
+typedef struct {
+  size_t offset; /* bytes from the start of the workspace (256-byte aligned) */
+  size_t bytes;
+} sage_span;
+
+/* Byte layout of every intermediate buffer inside one workspace. */
+typedef struct {
+  int64_t n_pad, n_qblocks, q_groups, k_groups;
+  sage_span q_codes, q_scale, q_mean, k_codes, k_scale, k_mean, bias, k_partial;
+  sage_span v_codes, v_scale, v_mean, v_partial;
+  size_t total_bytes;
+} sage_layout;
+
+/* Version of the buffer layouts and group maps (SAGE_ABI_VERSION). */
+SAGE_API int sage_abi_version(void);
+
+/* Fill *p with the defaults listed in sage_params. */
+SAGE_API void sage_params_default(sage_params* p);
+
+/* Host only.  Sizes and offsets of all intermediate buffers for this problem. */
+SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_params* p, sage_layout* out);
+
+/* Host only.  Point the buffer structs into a workspace laid out by
+ * sage_workspace_layout (ws must be 256-byte aligned, ws_bytes >= total). */
+SAGE_API sage_status sage_bind_workspace(const sage_layout* lay, void* ws, size_t ws_bytes,
+                                         sage_qk_buffers* qk, sage_v_buffers* vb);
+
+/* Smooth and quantize Q and K (SageAttention2 abstract: smoothing, INT4/INT8
+ * Q and K; SageAttention2++ summary 2.1: per-block scales for Q and K).
+ * Writes every field of *out (all must be non-NULL device pointers).
+ * Codes, scales and means follow fp32 arithmetic with round-to-nearest-even
+ * and a fixed pairwise summation tree in token order, so they are exactly
+ * reproducible. */
+SAGE_API sage_status sage_quant_qk(const void* q, const void* k, const sage_shape* s, const sage_params* p,
+                                   const sage_qk_buffers* out, void* stream);
+
+/* Smooth V by its token mean and encode V' to FP8 E4M3 with per-channel
+ * scales (SageAttention2 abstract: FP8 V and V smoothing; SageAttention2++
+ * summary 2.1: per-channel scaling of V). */
+SAGE_API sage_status sage_quant_v(const void* v, const sage_shape* s, const sage_params* p,
+                                  const sage_v_buffers* out, void* stream);
+
+/* Attention on the quantized buffers (SageAttention2++ summary, "2.
+ * Preliminary": FlashAttention-based tiled online softmax; INT8 matrix cores
+ * for QK^T, FP8 matrix cores for P~V).  causal != 0 masks key j > query i.
+ * o: [B, H, N, d] of the shape's dtype with element strides o_stride[0..2]
+ * (multiples of 8; 16-byte aligned pointer). */
+SAGE_API sage_status sage_attn_fwd(const sage_qk_buffers* qk, const sage_v_buffers* vb, const sage_shape* s,
+                                   const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                                   void* stream);
+
+/* The plug-and-play call: sage_quant_qk, sage_quant_v and sage_attn_fwd in
+ * order, with every intermediate buffer inside `workspace` (layout from
+ * sage_workspace_layout; 256-byte aligned; ws_bytes >= total_bytes). */
+SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, const sage_shape* s,
+                               const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+SAGE_API const char* sage_status_str(int status);
+
+/* Thread-local message for the last failed call on this thread ("" if none). */
+SAGE_API const char* sage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H_ */

@@ -1,0 +1,141 @@
+"""Torch-facing wrappers of the C ABI (memory and streams only).
+
+PyTorch provides device memory and the current HIP stream; the wrappers pass
+raw pointers, sizes and the stream to libsage.so and return views of the
+buffers it wrote.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float16: L.SAGE_F16, torch.bfloat16: L.SAGE_BF16}
+
+
+def make_params(qk_bits: int = 8, gran: str = "thread", smooth_q: bool = True, smooth_k: bool = True,
+                smooth_v: bool = True, p_range: float = 448.0, v_range: float = 448.0,
+                sm_scale: float = 0.0) -> L.Params:
+    if gran not in L.GRAN:
+        raise ValueError(f"granularity must be one of {sorted(L.GRAN)}")
+    return L.Params(int(qk_bits), L.GRAN[gran], int(bool(smooth_q)), int(bool(smooth_k)), int(bool(smooth_v)),
+                    float(p_range), float(v_range), float(sm_scale))
+
+
+def _check_tensor(x: torch.Tensor, name: str):
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be float16 or bfloat16")
+    if x.stride(3) != 1:
+        raise ValueError(f"{name} must be contiguous in d")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> L.Shape:
+    for x, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(x, n)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    B, H, N, d = q.shape
+    return L.Shape(B, H, N, d, _DTYPES[q.dtype], 0, L.c_i64_3(*q.stride()[:3]), L.c_i64_3(*k.stride()[:3]),
+                   L.c_i64_3(*v.stride()[:3]))
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Workspace:
+    """One device allocation holding every intermediate buffer, with typed views."""
+
+    def __init__(self, shape: L.Shape, params: L.Params, device):
+        lay = L.Layout()
+        L.check(L.lib().sage_workspace_layout(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(lay)))
+        self.layout = lay
+        self.shape = (shape.B, shape.H, shape.N, shape.d)
+        self.tensor = torch.empty(lay.total_bytes + 256, dtype=torch.uint8, device=device)
+        base = self.tensor.data_ptr()
+        self._pad = (-base) % 256
+        self.qk = L.QKBuffers()
+        self.vb = L.VBuffers()
+        L.check(L.lib().sage_bind_workspace(ctypes.byref(lay), ctypes.c_void_p(base + self._pad),
+                                            ctypes.c_size_t(lay.total_bytes), ctypes.byref(self.qk),
+                                            ctypes.byref(self.vb)))
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr() + self._pad
+
+    @property
+    def nbytes(self) -> int:
+        return self.layout.total_bytes
+
+    def view(self, name: str) -> torch.Tensor:
+        """Typed view of one buffer, shaped as include/sage.h documents it."""
+        B, H, N, d = self.shape
+        lay = self.layout
+        n_pad, nblk = lay.n_pad, lay.n_qblocks
+        sp = getattr(lay, name)
+        raw = self.tensor[self._pad + sp.offset: self._pad + sp.offset + sp.bytes]
+        shapes = {
+            "q_codes": (torch.int8, (B, H, n_pad, d)),
+            "k_codes": (torch.int8, (B, H, n_pad, d)),
+            "q_scale": (torch.float32, (B, H, lay.q_groups)),
+            "k_scale": (torch.float32, (B, H, lay.k_groups)),
+            "q_mean": (torch.float32, (B, H, nblk, d)),
+            "k_mean": (torch.float32, (B, H, d)),
+            "bias": (torch.float32, (B, H, nblk, n_pad)),
+            "k_partial": (torch.float32, (B, H, nblk, d)),
+            "v_codes": (torch.uint8, (B, H, d, n_pad)),
+            "v_scale": (torch.float32, (B, H, d)),
+            "v_mean": (torch.float32, (B, H, d)),
+            "v_partial": (torch.float32, (B, H, nblk, 3, d)),
+        }
+        dt, shp = shapes[name]
+        return raw.view(dt).view(shp)
+
+
+def quant_qk(q, k, v_for_shape, params: L.Params, ws: Workspace, shape: L.Shape = None):
+    shape = shape or make_shape(q, k, v_for_shape)
+    L.check(L.lib().sage_quant_qk(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.byref(shape),
+                                  ctypes.byref(params), ctypes.byref(ws.qk), ctypes.c_void_p(_stream(q.device))))
+
+
+def quant_v(v, params: L.Params, ws: Workspace, shape: L.Shape):
+    L.check(L.lib().sage_quant_v(ctypes.c_void_p(v.data_ptr()), ctypes.byref(shape), ctypes.byref(params),
+                                 ctypes.byref(ws.vb), ctypes.c_void_p(_stream(v.device))))
+
+
+def _out_strides(o: torch.Tensor):
+    return (ctypes.c_int64 * 3)(*o.stride()[:3])
+
+
+def attn_fwd(ws: Workspace, shape: L.Shape, params: L.Params, causal: bool, out: torch.Tensor):
+    _check_tensor(out, "out")
+    L.check(L.lib().sage_attn_fwd(ctypes.byref(ws.qk), ctypes.byref(ws.vb), ctypes.byref(shape), ctypes.byref(params),
+                                  int(bool(causal)), ctypes.c_void_p(out.data_ptr()), _out_strides(out),
+                                  ctypes.c_void_p(_stream(out.device))))
+
+
+def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, out: torch.Tensor = None,
+         workspace: Workspace = None, **kw) -> torch.Tensor:
+    """Plug-and-play quantized attention: O = softmax(sm_scale Q K^T [+ causal mask]) V.
+
+    Keyword arguments are those of ``make_params``.  Returns ``out`` (allocated
+    like ``q`` when not given).
+    """
+    params = make_params(**kw)
+    shape = make_shape(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out")
+    ws = workspace or Workspace(shape, params, q.device)
+    L.check(L.lib().sage_attn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                              ctypes.c_void_p(v.data_ptr()), ctypes.byref(shape), ctypes.byref(params),
+                              int(bool(causal)), ctypes.c_void_p(out.data_ptr()), _out_strides(out),
+                              ctypes.c_void_p(ws.ptr), ctypes.c_size_t(ws.nbytes), ctypes.c_void_p(_stream(q.device))))
+    return out

@@ -1,0 +1,265 @@
+// Host side of the C ABI declared in include/sage.h: argument validation,
+// buffer layout and dispatch to the gfx950 kernels.  Every check runs before
+// the first launch, so a call that fails has enqueued nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <initializer_list>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sage.h"
+#include "sage_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sage_status fail(sage_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sage_status ok() {
+  g_err[0] = '\0';
+  return SAGE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+sage_status check_params(const sage_params* p) {
+  if (!p) return fail(SAGE_EINVAL, "params is NULL");
+  if (p->qk_bits != 8 && p->qk_bits != 4) return fail(SAGE_EUNSUPPORTED, "qk_bits must be 8 or 4 (got %d)", p->qk_bits);
+  if (p->gran < SAGE_GRAN_THREAD || p->gran > SAGE_GRAN_BLOCK) return fail(SAGE_EINVAL, "unknown granularity %d", p->gran);
+  for (int f : {p->smooth_q, p->smooth_k, p->smooth_v})
+    if (f != 0 && f != 1) return fail(SAGE_EINVAL, "smoothing flags must be 0 or 1");
+  if (!(p->p_range > 0.f && p->p_range <= 448.f)) return fail(SAGE_EINVAL, "p_range must be in (0, 448]");
+  if (!(p->v_range > 0.f && p->v_range <= 448.f)) return fail(SAGE_EINVAL, "v_range must be in (0, 448]");
+  if (!(p->sm_scale >= 0.f) || !std::isfinite(p->sm_scale)) return fail(SAGE_EINVAL, "sm_scale must be finite and >= 0");
+  return SAGE_OK;
+}
+
+sage_status check_shape(const sage_shape* s) {
+  if (!s) return fail(SAGE_EINVAL, "shape is NULL");
+  if (s->B < 1 || s->H < 1) return fail(SAGE_EINVAL, "B and H must be >= 1");
+  if (s->B * s->H > 65535) return fail(SAGE_EUNSUPPORTED, "B*H must be <= 65535");
+  if (s->N < 1 || s->N > (1 << 20)) return fail(SAGE_EUNSUPPORTED, "N must be in [1, 2^20] (got %lld)", (long long)s->N);
+  if (s->d != 64 && s->d != 128) return fail(SAGE_EUNSUPPORTED, "head dim d must be 64 or 128 (got %lld)", (long long)s->d);
+  if (s->dtype != SAGE_F16 && s->dtype != SAGE_BF16) return fail(SAGE_EINVAL, "dtype must be SAGE_F16 or SAGE_BF16");
+  const int64_t* st[3] = {s->q_stride, s->k_stride, s->v_stride};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (st[i][j] <= 0 || st[i][j] % 8 != 0) return fail(SAGE_EINVAL, "strides must be positive multiples of 8 elements");
+  return SAGE_OK;
+}
+
+sage::Problem make_problem(const sage_shape* s, const sage_params* p) {
+  sage::Problem pr;
+  pr.B = static_cast<int>(s->B);
+  pr.H = static_cast<int>(s->H);
+  pr.N = static_cast<int>(s->N);
+  pr.D = static_cast<int>(s->d);
+  pr.n_pad = static_cast<int>((s->N + 127) / 128 * 128);
+  pr.nblk = pr.n_pad / 128;
+  pr.bf16 = s->dtype == SAGE_BF16;
+  pr.qmax = p->qk_bits == 8 ? 127 : 7;
+  pr.gran = p->gran;
+  pr.smooth_q = p->smooth_q;
+  pr.smooth_k = p->smooth_k;
+  pr.smooth_v = p->smooth_v;
+  pr.p_range = p->p_range;
+  pr.v_range = p->v_range;
+  pr.sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  return pr;
+}
+
+sage_status check_qk_buffers(const sage_qk_buffers* b) {
+  if (!b) return fail(SAGE_EINVAL, "qk buffers is NULL");
+  const void* ptrs[] = {b->q_codes, b->q_scale, b->q_mean, b->k_codes, b->k_scale, b->k_mean, b->bias, b->k_partial};
+  for (const void* q : ptrs) {
+    if (!q) return fail(SAGE_EINVAL, "a qk buffer pointer is NULL");
+    if (!aligned(q, 16)) return fail(SAGE_EINVAL, "qk buffers must be 16-byte aligned");
+  }
+  return SAGE_OK;
+}
+
+sage_status check_v_buffers(const sage_v_buffers* b) {
+  if (!b) return fail(SAGE_EINVAL, "v buffers is NULL");
+  const void* ptrs[] = {b->v_codes, b->v_scale, b->v_mean, b->v_partial};
+  for (const void* q : ptrs) {
+    if (!q) return fail(SAGE_EINVAL, "a v buffer pointer is NULL");
+    if (!aligned(q, 16)) return fail(SAGE_EINVAL, "v buffers must be 16-byte aligned");
+  }
+  return SAGE_OK;
+}
+
+sage_status check_tensor(const void* p, const char* name) {
+  if (!p) return fail(SAGE_EINVAL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(SAGE_EINVAL, "%s must be 16-byte aligned", name);
+  return SAGE_OK;
+}
+
+sage_status check_out(const void* o, const int64_t* os) {
+  sage_status st = check_tensor(o, "o");
+  if (st) return st;
+  if (!os) return fail(SAGE_EINVAL, "o_stride is NULL");
+  for (int j = 0; j < 3; ++j)
+    if (os[j] <= 0 || os[j] % 8 != 0) return fail(SAGE_EINVAL, "o strides must be positive multiples of 8 elements");
+  return SAGE_OK;
+}
+
+sage_status launch_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SAGE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+SAGE_API int sage_abi_version(void) { return SAGE_ABI_VERSION; }
+
+SAGE_API void sage_params_default(sage_params* p) {
+  if (!p) return;
+  p->qk_bits = 8;
+  p->gran = SAGE_GRAN_THREAD;
+  p->smooth_q = 1;
+  p->smooth_k = 1;
+  p->smooth_v = 1;
+  p->p_range = 448.f;
+  p->v_range = 448.f;
+  p->sm_scale = 0.f;
+}
+
+SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_params* p, sage_layout* out) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p))) return st;
+  if (!out) return fail(SAGE_EINVAL, "layout output is NULL");
+  const int64_t BH = s->B * s->H, D = s->d;
+  const int64_t n_pad = (s->N + 127) / 128 * 128, nblk = n_pad / 128;
+  const int64_t gq = p->gran == SAGE_GRAN_THREAD ? n_pad : (p->gran == SAGE_GRAN_WARP ? n_pad / 32 : nblk);
+  const int64_t gk = p->gran == SAGE_GRAN_THREAD ? n_pad / 16 : n_pad / 64;
+  sage_layout L;
+  memset(&L, 0, sizeof(L));
+  L.n_pad = n_pad;
+  L.n_qblocks = nblk;
+  L.q_groups = gq;
+  L.k_groups = gk;
+  size_t off = 0;
+  auto put = [&](sage_span& sp, int64_t bytes) {
+    sp.offset = off;
+    sp.bytes = static_cast<size_t>(bytes);
+    off = round_up(off + sp.bytes, 256);
+  };
+  put(L.q_codes, BH * n_pad * D);
+  put(L.q_scale, BH * gq * 4);
+  put(L.q_mean, BH * nblk * D * 4);
+  put(L.k_codes, BH * n_pad * D);
+  put(L.k_scale, BH * gk * 4);
+  put(L.k_mean, BH * D * 4);
+  put(L.bias, BH * nblk * n_pad * 4);
+  put(L.k_partial, BH * nblk * D * 4);
+  put(L.v_codes, BH * D * n_pad);
+  put(L.v_scale, BH * D * 4);
+  put(L.v_mean, BH * D * 4);
+  put(L.v_partial, BH * nblk * 3 * D * 4);
+  L.total_bytes = off;
+  *out = L;
+  return ok();
+}
+
+SAGE_API sage_status sage_bind_workspace(const sage_layout* L, void* ws, size_t ws_bytes, sage_qk_buffers* qk,
+                                         sage_v_buffers* vb) {
+  if (!L || !qk || !vb) return fail(SAGE_EINVAL, "NULL argument");
+  if (!ws) return fail(SAGE_EINVAL, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(SAGE_EINVAL, "workspace must be 256-byte aligned");
+  if (ws_bytes < L->total_bytes)
+    return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", ws_bytes, L->total_bytes);
+  char* base = static_cast<char*>(ws);
+  qk->q_codes = reinterpret_cast<int8_t*>(base + L->q_codes.offset);
+  qk->q_scale = reinterpret_cast<float*>(base + L->q_scale.offset);
+  qk->q_mean = reinterpret_cast<float*>(base + L->q_mean.offset);
+  qk->k_codes = reinterpret_cast<int8_t*>(base + L->k_codes.offset);
+  qk->k_scale = reinterpret_cast<float*>(base + L->k_scale.offset);
+  qk->k_mean = reinterpret_cast<float*>(base + L->k_mean.offset);
+  qk->bias = reinterpret_cast<float*>(base + L->bias.offset);
+  qk->k_partial = reinterpret_cast<float*>(base + L->k_partial.offset);
+  vb->v_codes = reinterpret_cast<uint8_t*>(base + L->v_codes.offset);
+  vb->v_scale = reinterpret_cast<float*>(base + L->v_scale.offset);
+  vb->v_mean = reinterpret_cast<float*>(base + L->v_mean.offset);
+  vb->v_partial = reinterpret_cast<float*>(base + L->v_partial.offset);
+  return ok();
+}
+
+SAGE_API sage_status sage_quant_qk(const void* q, const void* k, const sage_shape* s, const sage_params* p,
+                                   const sage_qk_buffers* out, void* stream) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p)) || (st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
+      (st = check_qk_buffers(out)))
+    return st;
+  const sage::Problem pr = make_problem(s, p);
+  const sage::TensorView qv{q, s->q_stride[0], s->q_stride[1], s->q_stride[2]};
+  const sage::TensorView kv{k, s->k_stride[0], s->k_stride[1], s->k_stride[2]};
+  return launch_result(sage::launch_quant_qk(pr, qv, kv, *out, static_cast<hipStream_t>(stream)), "sage_quant_qk");
+}
+
+SAGE_API sage_status sage_quant_v(const void* v, const sage_shape* s, const sage_params* p, const sage_v_buffers* out,
+                                  void* stream) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p)) || (st = check_tensor(v, "v")) || (st = check_v_buffers(out)))
+    return st;
+  const sage::Problem pr = make_problem(s, p);
+  const sage::TensorView vv{v, s->v_stride[0], s->v_stride[1], s->v_stride[2]};
+  return launch_result(sage::launch_quant_v(pr, vv, *out, static_cast<hipStream_t>(stream)), "sage_quant_v");
+}
+
+SAGE_API sage_status sage_attn_fwd(const sage_qk_buffers* qk, const sage_v_buffers* vb, const sage_shape* s,
+                                   const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                                   void* stream) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p)) || (st = check_qk_buffers(qk)) || (st = check_v_buffers(vb)) ||
+      (st = check_out(o, o_stride)))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  const sage::Problem pr = make_problem(s, p);
+  return launch_result(sage::launch_attn_fwd(pr, *qk, *vb, causal, o, o_stride, static_cast<hipStream_t>(stream)),
+                       "sage_attn_fwd");
+}
+
+SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, const sage_shape* s, const sage_params* p,
+                               int causal, void* o, const int64_t o_stride[3], void* workspace, size_t ws_bytes,
+                               void* stream) {
+  sage_status st;
+  sage_layout L;
+  if ((st = sage_workspace_layout(s, p, &L))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_out(o, o_stride)))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  sage_qk_buffers qk;
+  sage_v_buffers vb;
+  if ((st = sage_bind_workspace(&L, workspace, ws_bytes, &qk, &vb))) return st;
+  if ((st = sage_quant_qk(q, k, s, p, &qk, stream))) return st;
+  if ((st = sage_quant_v(v, s, p, &vb, stream))) return st;
+  return sage_attn_fwd(&qk, &vb, s, p, causal, o, o_stride, stream);
+}
+
+SAGE_API const char* sage_status_str(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_EINVAL: return "invalid argument";
+    case SAGE_EUNSUPPORTED: return "unsupported";
+    case SAGE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+SAGE_API const char* sage_last_error(void) { return g_err; }
+
+}  // extern "C"

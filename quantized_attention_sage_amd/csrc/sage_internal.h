@@ -1,0 +1,34 @@
+// Internal launch interface between the C ABI (sage_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sage.h"
+
+namespace sage {
+
+constexpr int kQBlock = 128;   // queries per attention work-group and per Q-mean block
+constexpr int kKTile = 128;    // keys per attention tile (one online-softmax update)
+
+struct TensorView {
+  const void* ptr;
+  int64_t sB, sH, sN;  // element strides
+};
+
+struct Problem {
+  int B, H, N, D, n_pad, nblk;   // nblk = n_pad / 128
+  int bf16;                      // 1: bfloat16 inputs/outputs, 0: float16
+  int qmax;
+  int gran;                      // sage_gran
+  int smooth_q, smooth_k, smooth_v;
+  float p_range, v_range, sm_scale;
+};
+
+hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
+                           hipStream_t st);
+hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st);
+hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
+                           void* o, const int64_t o_stride[3], hipStream_t st);
+
+}  // namespace sage

@@ -1,0 +1,114 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare with the oracle.  Inputs come from the shared seeded generators; no
+expected value comes from the HIP path."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from oracle.attention import round_output
+
+BUFFERS = ("q_codes", "q_scale", "q_mean", "k_codes", "k_scale", "k_mean", "bias",
+           "v_codes", "v_scale", "v_mean")
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(name):
+    import torch
+    return {"bf16": torch.bfloat16, "fp16": torch.float16}[name]
+
+
+def to_device(x: np.ndarray, dtype: str, layout: str = "bhnd"):
+    """Upload exactly-representable float32 values as fp16/bf16.
+
+    layout "bnhd" stores the tensor as [B, N, H, d] and returns the
+    [B, H, N, d] view (non-contiguous strides through the ABI).
+    """
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch_dtype(dtype))
+    if layout == "bnhd":
+        t = t.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    else:
+        t = t.cuda()
+    return t
+
+
+def run_sage(q, k, v, dtype, causal, qk_bits=8, gran="thread", smooth=(True, True, True), p_range=448.0,
+             v_range=448.0, layout="bhnd", download=BUFFERS):
+    import torch
+    from quantized_attention_sage_amd import api
+    qt, kt, vt = (to_device(x, dtype, layout) for x in (q, k, v))
+    params = api.make_params(qk_bits=qk_bits, gran=gran, smooth_q=smooth[0], smooth_k=smooth[1], smooth_v=smooth[2],
+                             p_range=p_range, v_range=v_range)
+    shape = api.make_shape(qt, kt, vt)
+    ws = api.Workspace(shape, params, qt.device)
+    api.quant_qk(qt, kt, vt, params, ws, shape)
+    api.quant_v(vt, params, ws, shape)
+    out = torch.empty_like(qt)
+    api.attn_fwd(ws, shape, params, causal, out)
+    torch.cuda.synchronize()
+    res = {name: ws.view(name).cpu().numpy() for name in download}
+    res["out"] = out.float().cpu().numpy()
+    return res
+
+
+def unpermute_v(vc: np.ndarray) -> np.ndarray:
+    """[B,H,d,n_pad] permuted E4M3 codes -> [B,H,n_pad,d] natural order.
+
+    Within each 64-key group, byte 32h + t holds key 32(t/16) + 8((t%16)/4) + 4h + t%4
+    (the layout include/sage.h documents)."""
+    n_pad = vc.shape[-1]
+    pos = np.empty(64, np.int64)
+    for hh in range(2):
+        for t in range(32):
+            pos[32 * (t // 16) + 8 * ((t % 16) // 4) + 4 * hh + t % 4] = 32 * hh + t
+    keys = np.arange(n_pad)
+    idx = (keys // 64) * 64 + pos[keys % 64]
+    return np.ascontiguousarray(np.swapaxes(vc[..., idx], -1, -2))
+
+
+def bits(x):
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def assert_quant_bit_exact(gpu: dict, qk: dict, vq: dict):
+    np.testing.assert_array_equal(gpu["q_codes"], qk["q_codes"], err_msg="q codes")
+    np.testing.assert_array_equal(gpu["k_codes"], qk["k_codes"], err_msg="k codes")
+    np.testing.assert_array_equal(bits(gpu["q_scale"]), bits(qk["q_scale"]), err_msg="q scales")
+    np.testing.assert_array_equal(bits(gpu["k_scale"]), bits(qk["k_scale"]), err_msg="k scales")
+    np.testing.assert_array_equal(bits(gpu["q_mean"]), bits(qk["q_mean"]), err_msg="q means")
+    np.testing.assert_array_equal(bits(gpu["k_mean"]), bits(qk["k_mean"]), err_msg="k means")
+    np.testing.assert_array_equal(unpermute_v(gpu["v_codes"]), vq["v_codes"], err_msg="v codes")
+    np.testing.assert_array_equal(bits(gpu["v_scale"]), bits(vq["v_scale"]), err_msg="v scales")
+    np.testing.assert_array_equal(bits(gpu["v_mean"]), bits(vq["v_mean"]), err_msg="v means")
+
+
+def bias_tolerance_ok(gpu_bias, ref_bias, q_mean, k_smoothed):
+    """The bias runs on bf16 matrix cores with a 3-product hi/lo split (about
+    2^-16 relative per product): |err| <= 2^-14 * sum_c |mu_c| |K'_jc| + tiny."""
+    scale = np.einsum("bhqc,bhjc->bhqj", np.abs(q_mean).astype(np.float64), np.abs(k_smoothed).astype(np.float64))
+    err = np.abs(gpu_bias.astype(np.float64) - ref_bias.astype(np.float64))
+    return np.all(err <= 2.0 ** -14 * scale + 1e-30), float((err / (scale + 1e-30)).max())
+
+
+def output_tolerance(v: np.ndarray, emul: np.ndarray, dtype: str) -> np.ndarray:
+    """2e-3 * max|V| (the bar against the emulation) plus half an output ulp
+    for the final rounding of O to fp16/bf16."""
+    mant = 8 if dtype == "bf16" else 11
+    a = np.abs(emul)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - (mant - 1))
+    return 2e-3 * np.abs(v).max() + 0.5 * ulp
+
+
+def check_output(gpu_out, emul, v, dtype):
+    tol = output_tolerance(v, emul, dtype)
+    keep = ~np.isnan(emul)
+    err = np.abs(gpu_out - emul)
+    bad = keep & (err > tol)
+    return int(bad.sum()), float(np.nanmax(np.where(keep, err, np.nan))), float(2e-3 * np.abs(v).max())

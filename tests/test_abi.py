@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every symbol include/sage.h declares, and its
+host-side logic (layout, binding, validation) behaves as documented.  Nothing
+here launches a kernel, so it runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_attention_sage_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"SAGE_API\s+[\w\s\*]+?\b(sage_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_symbols())
+    assert {"sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attn"} <= names
+    assert names == set(L.EXPORTS), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (sage_\w+)", out))
+    assert exported == set(declared_symbols())
+
+
+def test_abi_version_matches_header():
+    v = int(re.search(r"#define SAGE_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.lib().sage_abi_version() == v
+
+
+def _shape(B=1, H=2, N=1000, d=128, dtype=L.SAGE_BF16, stride=None):
+    st = stride or (H * N * d, N * d, d)
+    return L.Shape(B, H, N, d, dtype, 0, L.c_i64_3(*st), L.c_i64_3(*st), L.c_i64_3(*st))
+
+
+def _params(**kw):
+    p = L.Params()
+    L.lib().sage_params_default(ctypes.byref(p))
+    for k_, v_ in kw.items():
+        setattr(p, k_, v_)
+    return p
+
+
+def test_defaults():
+    p = _params()
+    assert (p.qk_bits, p.gran, p.smooth_q, p.smooth_k, p.smooth_v) == (8, 0, 1, 1, 1)
+    assert (p.p_range, p.v_range, p.sm_scale) == (448.0, 448.0, 0.0)
+
+
+@pytest.mark.parametrize("gran,gq,gk", [(0, 1024, 64), (1, 32, 16), (2, 8, 16)])
+def test_layout_sizes(gran, gq, gk):
+    B, H, N, d = 2, 3, 1000, 128
+    n_pad, nblk = 1024, 8
+    lay = L.Layout()
+    assert L.lib().sage_workspace_layout(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(_params(gran=gran)),
+                                         ctypes.byref(lay)) == L.SAGE_OK
+    assert (lay.n_pad, lay.n_qblocks, lay.q_groups, lay.k_groups) == (n_pad, nblk, gq, gk)
+    BH = B * H
+    expect = {"q_codes": BH * n_pad * d, "k_codes": BH * n_pad * d, "q_scale": BH * gq * 4, "k_scale": BH * gk * 4,
+              "q_mean": BH * nblk * d * 4, "k_mean": BH * d * 4, "bias": BH * nblk * n_pad * 4,
+              "k_partial": BH * nblk * d * 4, "v_codes": BH * d * n_pad, "v_scale": BH * d * 4,
+              "v_mean": BH * d * 4, "v_partial": BH * nblk * 3 * d * 4}
+    spans = sorted((getattr(lay, n).offset, getattr(lay, n).bytes, n) for n in L.SPANS)
+    for (off, size, name) in spans:
+        assert size == expect[name], name
+        assert off % 256 == 0
+    for (a, b) in zip(spans, spans[1:]):
+        assert a[0] + a[1] <= b[0]
+    assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
+
+
+def test_bind_workspace_checks():
+    lib = L.lib()
+    lay = L.Layout()
+    lib.sage_workspace_layout(ctypes.byref(_shape()), ctypes.byref(_params()), ctypes.byref(lay))
+    qk, vb = L.QKBuffers(), L.VBuffers()
+    base = 1 << 40   # never dereferenced
+    assert lib.sage_bind_workspace(ctypes.byref(lay), ctypes.c_void_p(base + 16), lay.total_bytes,
+                                   ctypes.byref(qk), ctypes.byref(vb)) == L.SAGE_EINVAL
+    assert lib.sage_bind_workspace(ctypes.byref(lay), ctypes.c_void_p(base), lay.total_bytes - 1,
+                                   ctypes.byref(qk), ctypes.byref(vb)) == L.SAGE_EINVAL
+    assert b"too small" in lib.sage_last_error()
+    assert lib.sage_bind_workspace(ctypes.byref(lay), ctypes.c_void_p(base), lay.total_bytes,
+                                   ctypes.byref(qk), ctypes.byref(vb)) == L.SAGE_OK
+    assert qk.bias == base + lay.bias.offset and vb.v_codes == base + lay.v_codes.offset
+
+
+BAD_SHAPES = [
+    dict(d=96), dict(N=0), dict(N=(1 << 20) + 1), dict(B=0), dict(dtype=7),
+    dict(stride=(1000 * 128 * 2, 1000 * 128, 100)),      # N stride not a multiple of 8
+]
+
+
+@pytest.mark.parametrize("bad", BAD_SHAPES)
+def test_bad_shapes_are_rejected(bad):
+    lay = L.Layout()
+    st = L.lib().sage_workspace_layout(ctypes.byref(_shape(**bad)), ctypes.byref(_params()), ctypes.byref(lay))
+    assert st in (L.SAGE_EINVAL, L.SAGE_EUNSUPPORTED)
+    assert L.lib().sage_last_error() != b""
+
+
+BAD_PARAMS = [dict(qk_bits=6), dict(gran=3), dict(smooth_q=2), dict(p_range=0.0), dict(p_range=449.0),
+              dict(v_range=-1.0), dict(sm_scale=-0.5), dict(sm_scale=float("inf"))]
+
+
+@pytest.mark.parametrize("bad", BAD_PARAMS)
+def test_bad_params_are_rejected(bad):
+    lay = L.Layout()
+    st = L.lib().sage_workspace_layout(ctypes.byref(_shape()), ctypes.byref(_params(**bad)), ctypes.byref(lay))
+    assert st in (L.SAGE_EINVAL, L.SAGE_EUNSUPPORTED)
+
+
+def test_entry_points_validate_before_launching():
+    lib = L.lib()
+    sh, p = _shape(), _params()
+    fake = ctypes.c_void_p(1 << 40)
+    qk = L.QKBuffers(*([1 << 40] * 8))
+    vb = L.VBuffers(*([1 << 40] * 4))
+    strides = (ctypes.c_int64 * 3)(256000, 128000, 128)
+    assert lib.sage_quant_qk(None, fake, ctypes.byref(sh), ctypes.byref(p), ctypes.byref(qk), None) == L.SAGE_EINVAL
+    assert lib.sage_quant_qk(fake, ctypes.c_void_p((1 << 40) + 2), ctypes.byref(sh), ctypes.byref(p),
+                             ctypes.byref(qk), None) == L.SAGE_EINVAL     # misaligned
+    qk_null = L.QKBuffers(*([1 << 40] * 7 + [0]))
+    assert lib.sage_quant_qk(fake, fake, ctypes.byref(sh), ctypes.byref(p), ctypes.byref(qk_null),
+                             None) == L.SAGE_EINVAL
+    assert lib.sage_quant_v(fake, ctypes.byref(sh), ctypes.byref(_params(v_range=500.0)), ctypes.byref(vb),
+                            None) == L.SAGE_EINVAL
+    assert lib.sage_attn_fwd(ctypes.byref(qk), ctypes.byref(vb), ctypes.byref(sh), ctypes.byref(p), 2, fake,
+                             strides, None) == L.SAGE_EINVAL                # causal must be 0/1
+    bad_strides = (ctypes.c_int64 * 3)(256000, 128000, 130)
+    assert lib.sage_attn_fwd(ctypes.byref(qk), ctypes.byref(vb), ctypes.byref(sh), ctypes.byref(p), 0, fake,
+                             bad_strides, None) == L.SAGE_EINVAL
+    assert lib.sage_attn(fake, fake, fake, ctypes.byref(sh), ctypes.byref(p), 0, fake, strides, fake, 10,
+                         None) == L.SAGE_EINVAL                            # workspace too small
+    assert lib.sage_status_str(L.SAGE_EUNSUPPORTED) == b"unsupported"
