@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload target] [--gpus 1]
+
+One step = sage_quant_qk + sage_quant_v + sage_attn_fwd over one batch of
+synthetic inputs already resident in HBM.  Prints ONE JSON line.  `value` is
+attention TOPS of the whole step: 4*B*H*N^2*d (halved when causal) divided by
+the step time.  `roofline` covers the attention kernel, timed with HIP events
+on the stream it is launched on.  `cpu_baseline` times the CPU oracle
+(quantisation emulation plus tiled attention emulation) on a bounded sample of
+the same workload and extrapolates per head.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = 5000.0      # MI355X dense INT8 and FP8 matrix peak (both 5.0 P/s)
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_counters.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn.hip", "sage_internal.h"):
+        with open(os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel changed since."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, sample_blocks: int = 24):
+    """Time the oracle on one head: quantisation of the head plus the tiled
+    emulation of `sample_blocks` query blocks, extrapolated to the workload."""
+    import numpy as np
+    import oracle
+    from oracle.quant import QuantParams
+    from quantized_attention_sage_amd.workloads import make_inputs, scaled
+
+    one = scaled(w, B=1, H=1)
+    q, k, v = make_inputs(one)
+    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran)
+    t0 = time.perf_counter()
+    qk = oracle.quant_qk(q, k, p, with_bias=False)
+    vq = oracle.quant_v(v, p)
+    t_quant = time.perf_counter() - t0
+    nqb = qk["n_pad"] // 128
+    picks = sorted(set(int(x) for x in np.linspace(0, nqb - 1, sample_blocks)))
+    t0 = time.perf_counter()
+    for qb in picks:
+        oracle.emulate_block(qk, vq, 0, 0, qb, w.causal)
+    t_blocks = time.perf_counter() - t0
+    if w.causal:   # block cost grows with its key count; scale by the mean over blocks
+        keys = [min(w.N, 128 * (qb + 1)) for qb in picks]
+        mean_keys = sum(min(w.N, 128 * (b + 1)) for b in range(nqb)) / nqb
+        per_block = t_blocks / sum(keys) * mean_keys
+    else:
+        per_block = t_blocks / len(picks)
+    t_total = w.B * w.H * (t_quant + nqb * per_block)
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max(blas) if blas else threads
+    except Exception:
+        pass
+    return {"value": w.ops / t_total / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": (f"one head of {w.name}: oracle quantisation of Q,K,V ({t_quant:.2f}s) + tiled emulation of "
+                       f"query blocks {picks} ({t_blocks:.2f}s), extrapolated to B*H heads x {nqb} blocks"),
+            "seconds_measured": round(t_quant + t_blocks, 2), "seconds_extrapolated": round(t_total, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="target")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from quantized_attention_sage_amd import api
+    from quantized_attention_sage_amd.workloads import WORKLOADS, make_inputs, describe
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    q, k, v = make_inputs(w)
+    qt, kt, vt = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
+    del q, k, v
+    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran)
+    shape = api.make_shape(qt, kt, vt)
+    ws = api.Workspace(shape, params, dev)
+    out = torch.empty_like(qt)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        api.quant_qk(qt, kt, vt, params, ws, shape)
+        if ev is not None:
+            ev[1].record(stream)
+        api.quant_v(vt, params, ws, shape)
+        if ev is not None:
+            ev[2].record(stream)
+        api.attn_fwd(ws, shape, params, w.causal, out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # Per-kernel-group durations with HIP events on the launch stream (separate pass).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    qk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    v_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    tops = w.ops / (ms_per_step * 1e-3) / 1e12
+    attn_tops = w.ops / (attn_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(w.name)
+    rec = {
+        "metric": "attention TOPS (4*B*H*N^2*d, halved if causal) of quant_qk + quant_v + attn_fwd",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 QK / fp8 PV (bf16 in/out)" if w.qk_bits == 8 else "int4-range QK / fp8 PV",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "io_dtype": w.dtype, "qk_bits": w.qk_bits, "granularity": w.gran},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 1), "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4),
+                     "ops_per_launch": w.ops},
+        "breakdown_ms": {"quant_qk": round(qk_ms, 4), "quant_v": round(v_ms, 4), "attn_fwd": round(attn_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
