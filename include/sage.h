@@ -93,7 +93,8 @@ typedef struct {
  *   k_codes  int8  [B, H, N_pad, d]
  *   k_scale  fp32  [B, H, Gk]         Gk = N_pad/16 (THREAD), N_pad/64 (WARP, BLOCK)
  *   k_mean   fp32  [B, H, d]
- *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j]; 0 for j >= N
+ *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j] * sm_scale * log2(e)
+ *            (the bias in the exp2 domain of the softmax); 0 for j >= N
  *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)   */
 typedef struct {
   int8_t* q_codes;

@@ -61,19 +61,113 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Work-group -> (head, query block).  Work-groups are dispatched round-robin
+// over the 8 XCDs (each with its own L2), so consecutive ids are regrouped to
+// give every XCD a contiguous run of (head, block) items: the K/V codes of one
+// head then stay in that XCD's L2 while its blocks run.  Causal runs visit the
+// blocks of a head from the last (longest) to the first.
+__device__ __forceinline__ void map_block(int id, int total, int nblk, int causal, int& bh, int& qb) {
+  constexpr int kXcd = 8;
+  int w = id;
+  if (total % kXcd == 0) w = (id % kXcd) * (total / kXcd) + id / kXcd;
+  bh = w / nblk;
+  qb = w % nblk;
+  if (causal) qb = nblk - 1 - qb;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* lds_ptr(void* p) { return (lds_void*)(p); }
+
+template <int D>
+struct TileBuf {
+  static constexpr int K_BYTES = 128 * D;          // K codes, 128 keys x D, rows swizzled
+  static constexpr int V_BYTES = D * 128;          // V codes, D channels x 128 keys, rows swizzled
+  static constexpr int B_BYTES = 128 * 4;          // bias of the 128 keys
+  static constexpr int S_BYTES = 64 * 4;           // K scales of the tile (8 or 2 used)
+  static constexpr int BYTES = K_BYTES + V_BYTES + B_BYTES + S_BYTES;
+};
+
+// Direct global->LDS copies of one key tile through buffer resources (raw
+// buffers: reads past num_records return zero instead of faulting).  Lane L of
+// a wave-wide copy always lands at (LDS base + 16 L), so each lane fetches the
+// chunk that belongs at its destination in the swizzled layout.  With chunk
+// p = 256 j + threadIdx.x, the swizzled column does not depend on j, so one
+// per-lane offset serves every copy of a stream and j moves only the scalar
+// offset (4096 j bytes of K rows, 32 j channel rows of V).
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t k, v, b, s;
+  uint32_t k_off, v_off, b_off;   // per-lane byte offsets for j = 0 and k0 = 0
+  uint32_t v_row;                 // bytes per V channel row (n_pad)
+  uint32_t s_per_tile;            // K scale groups per 128-key tile (8 or 2)
+};
+
+template <int D>
+__device__ __forceinline__ TileSrc make_tile_src(const int8_t* kbase, const uint8_t* vbase, const float* brow,
+                                                 const float* kscale, int n_scale, int n_pad, int t) {
+  constexpr int CPR = D / 16;
+  TileSrc s;
+  const uint32_t flags = 0x00020000u;   // raw 32-bit data format, no swizzle
+  s.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kbase), 0, n_pad * D, flags);
+  s.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase), 0, n_pad * D, flags);
+  s.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(brow), 0, n_pad * 4, flags);
+  s.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kscale), 0, n_scale * 4, flags);
+  s.s_per_tile = static_cast<uint32_t>(n_scale / (n_pad / 128));
+  const int r = t / CPR, pc = t % CPR;
+  s.k_off = static_cast<uint32_t>(r * D + 16 * swz<D>(r, pc));
+  const int ch = t >> 3, vc = t & 7;
+  s.v_off = static_cast<uint32_t>(ch * n_pad + 16 * swz<128>(ch, vc));
+  s.b_off = static_cast<uint32_t>(4 * t);
+  s.v_row = static_cast<uint32_t>(n_pad);
+  return s;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_tile(uint8_t* buf, const TileSrc& s, int k0, int w) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, lds_ptr(buf + (4 * j + w) * 1024), 16, s.k_off,
+                                             static_cast<uint32_t>(k0 * D + 4096 * j), 0, 0);
+  uint8_t* vb = buf + TileBuf<D>::K_BYTES;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.v, lds_ptr(vb + (4 * j + w) * 1024), 16, s.v_off,
+                                             static_cast<uint32_t>(k0) + 32u * j * s.v_row, 0, 0);
+  if (w < 2) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.b, lds_ptr(buf + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES + 256 * w),
+                                             4, s.b_off, static_cast<uint32_t>(4 * k0), 0, 0);
+  } else if (w == 2 && s.b_off - 512u < 4u * s.s_per_tile) {
+    // lanes 0 .. s_per_tile-1 of wave 2 copy the tile's K scales (lane l reads scale l)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        s.s, lds_ptr(buf + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES + TileBuf<D>::B_BYTES), 4, s.b_off - 512u,
+        static_cast<uint32_t>(4 * (k0 / 128) * s.s_per_tile), 0, 0);
+  }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = D / 32;  // 32-channel k-steps of the QK product
   constexpr int CT = D / 32;  // 32-channel tiles of the output
-  __shared__ __attribute__((aligned(16))) int8_t ks[128 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t vs[D * 128];
-  __shared__ float bs[128];
+  // Two distinct LDS objects (not halves of one array) so the compiler can see
+  // that reads of the current tile do not alias the copies into the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[TileBuf<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[TileBuf<D>::BYTES];
 
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, col = l & 31, hh = l >> 5;
-  const int bh = blockIdx.y;
-  const int qb = a.causal ? (a.nblk - 1 - static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
+  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, held in a scalar register
+  int bh, qb;
+  map_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), a.nblk, a.causal, bh, qb);
   const int q0 = qb * 128;
   const int qi = q0 + 32 * w + col;
+
+  const int key_end = a.causal ? min(a.N, q0 + 128) : a.N;
+  const int ntiles = (key_end + 127) / 128;
+  const int8_t* kbase = a.k_codes + static_cast<int64_t>(bh) * a.n_pad * D;
+  const uint8_t* vbase = a.v_codes + static_cast<int64_t>(bh) * D * a.n_pad;
+  const float* brow = a.bias + (static_cast<int64_t>(bh) * a.nblk + qb) * a.n_pad;
+  const int n_kscale = a.gran == SAGE_GRAN_THREAD ? a.n_pad / 16 : a.n_pad / 64;
+  const float* kscale = a.k_scale + static_cast<int64_t>(bh) * n_kscale;
+  const TileSrc src = make_tile_src<D>(kbase, vbase, brow, kscale, n_kscale, a.n_pad, t);
+  issue_tile<D>(buf0, src, 0, w);
 
   i32x4 qf[KS];
   {
@@ -98,29 +192,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  const int key_end = a.causal ? min(a.N, q0 + 128) : a.N;
-  const int ntiles = (key_end + 127) / 128;
-  const int8_t* kbase = a.k_codes + static_cast<int64_t>(bh) * a.n_pad * D;
-  const uint8_t* vbase = a.v_codes + static_cast<int64_t>(bh) * D * a.n_pad;
-  const float* brow = a.bias + (static_cast<int64_t>(bh) * a.nblk + qb) * a.n_pad;
-
-  for (int tt = 0; tt < ntiles; ++tt) {
+  auto step = [&](const int tt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
     const int k0 = tt * 128;
+    // This thread's copies of tile tt are complete; after the barrier everyone's
+    // are, and every wave has finished reading `nxt` (it held tile tt-1).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (tt + 1 < ntiles) issue_tile<D>(nxt, src, k0 + 128, w);
+
+    const int8_t* ks = reinterpret_cast<const int8_t*>(cur);
+    const uint8_t* vs = cur + TileBuf<D>::K_BYTES;
+    const float* bs = reinterpret_cast<const float*>(cur + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES);
+    const float* ksc = reinterpret_cast<const float*>(cur + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES +
+                                                      TileBuf<D>::B_BYTES);
+    float cs[4];
 #pragma unroll
-    for (int i = t; i < 128 * D / 16; i += 256) {
-      const int r = i / (D / 16), c = i % (D / 16);
-      const uint4 v = *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(k0 + r) * D + 16 * c);
-      *reinterpret_cast<uint4*>(ks + r * D + 16 * swz<D>(r, c)) = v;
-    }
-#pragma unroll
-    for (int i = t; i < D * 8; i += 256) {
-      const int c = i >> 3, p = i & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(c) * a.n_pad + k0 + 16 * p);
-      *reinterpret_cast<uint4*>(vs + c * 128 + 16 * swz<128>(c, p)) = v;
-    }
-    if (t < 128) bs[t] = brow[k0 + t] * a.scale_log2;
-    __syncthreads();
+    for (int st = 0; st < 4; ++st) cs[st] = dq2 * (a.gran == SAGE_GRAN_THREAD ? ksc[2 * st + hh] : ksc[st >> 1]);
 
     // S^T tile: 4 subtiles of 32 keys.
     i32x16 sacc[4];
@@ -136,25 +223,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 
-    float cs[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      float dk;
-      if (a.gran == SAGE_GRAN_THREAD) {
-        dk = a.k_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + 2 * (k0 / 32 + st) + hh];
-      } else {
-        dk = a.k_scale[static_cast<int64_t>(bh) * (a.n_pad / 64) + ((k0 + 32 * st) >> 6)];
-      }
-      cs[st] = dq2 * dk;
-    }
-
     float x[4][16];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
-        x[st][r] = static_cast<float>(sacc[st][r]) * cs[st] + bs[kl];
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 bv = *reinterpret_cast<const float4*>(bs + 32 * st + 8 * a4 + 4 * hh);
+        x[st][4 * a4 + 0] = static_cast<float>(sacc[st][4 * a4 + 0]) * cs[st] + bv.x;
+        x[st][4 * a4 + 1] = static_cast<float>(sacc[st][4 * a4 + 1]) * cs[st] + bv.y;
+        x[st][4 * a4 + 2] = static_cast<float>(sacc[st][4 * a4 + 2]) * cs[st] + bv.z;
+        x[st][4 * a4 + 3] = static_cast<float>(sacc[st][4 * a4 + 3]) * cs[st] + bv.w;
+        __builtin_amdgcn_sched_barrier(0);   // consume each bias quad before fetching the next
       }
     const bool need_mask = (k0 + 128 > a.N) || (a.causal && k0 + 127 > q0 + 32 * w);
     if (need_mask) {
@@ -173,10 +252,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[st][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mnew = fmaxf(m, mt);
-    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+    const float alpha = (m == mnew) ? 1.f : ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
     const float base = (mnew == -INFINITY) ? 0.f : mnew - a.log2_pr;
     float ps = 0.f;
-    uint32_t pk[4][4];
+    i32x8 pb[2];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -186,25 +265,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         const float p2 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 2] - base);
         const float p3 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 3] - base);
         ps += (p0 + p1) + (p2 + p3);
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
         v = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, v, true);
-        pk[st][q4] = static_cast<uint32_t>(v);
+        pb[st >> 1][4 * (st & 1) + q4] = v;
       }
     lsum = alpha * lsum + ps;
     m = mnew;
+    // Exact skip: when no row maximum of this wave moved, alpha == 1 everywhere.
+    if (!__all(alpha == 1.f)) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+    }
 
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      i32x8 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = static_cast<int>(pk[2 * kc][i]);
-        pb[4 + i] = static_cast<int>(pk[2 * kc + 1][i]);
-      }
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         const int ch = 32 * c + col;
@@ -215,9 +291,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         va[2] = static_cast<int>(v0.z); va[3] = static_cast<int>(v0.w);
         va[4] = static_cast<int>(v1.x); va[5] = static_cast<int>(v1.y);
         va[6] = static_cast<int>(v1.z); va[7] = static_cast<int>(v1.w);
-        oacc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[c], 0, 0, 0, 0, 0, 0);
+        oacc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[kc], oacc[c], 0, 0, 0, 0, 0, 0);
       }
     }
+  };
+  for (int tt = 0; tt < ntiles; tt += 2) {
+    step(tt, buf0, buf1);
+    if (tt + 1 < ntiles) step(tt + 1, buf1, buf0);
   }
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -262,7 +342,7 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.gran = p.gran; a.causal = causal ? 1 : 0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.log2_pr = log2f(p.p_range);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16>), dim3(p.nblk, p.B * p.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16>), dim3(p.nblk * p.B * p.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

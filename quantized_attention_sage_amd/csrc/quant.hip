@@ -162,6 +162,7 @@ struct QKArgs {
   int64_t qsB, qsH, qsN, ksB, ksH, ksN;
   sage_qk_buffers out;
   int H, N, n_pad, nblk, gran, qmax, smooth_q, smooth_k;
+  float scale_log2;  // sm_scale * log2(e): the bias is stored in the exp2 domain
 };
 
 // Pass 1, one work-group per (128-token block, head): Q block mean, Q codes and
@@ -257,7 +258,7 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 // Pass 2, one work-group per (128-key block, head): K' = K - mean, K codes and
 // scales, then the bias dS[qb, j] = mu_Q(qb) . K'_j for the block's keys and
 // every Q block, on the bf16 matrix cores with a three-product hi/lo split of
-// both operands (about 16 significant bits).
+// both operands (about 16 significant bits), stored times sm_scale * log2(e).
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
   const int ngk = k_groups_per_block(a.gran);
   quantize_block<D, false>(x, a.gran, a.qmax, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
                            a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
-  // quantize_block ends after a barrier, so khi/klo are complete here.
+  // quantize_block passed a barrier after khi/klo were written, so they are complete here.
 
   const int w = t / 64, l = t % 64, col = l & 31, hh = l >> 5;
   const int key = 32 * w + col;
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int qb = qb0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (qb < a.nblk) bias[static_cast<int64_t>(qb) * a.n_pad] = acc[i];
+      if (qb < a.nblk) bias[static_cast<int64_t>(qb) * a.n_pad] = acc[i] * a.scale_log2;
     }
   }
 }
@@ -487,6 +488,7 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.out = out;
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk;
   a.gran = p.gran; a.qmax = p.qmax; a.smooth_q = p.smooth_q; a.smooth_k = p.smooth_k;
+  a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
   hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((k_mean_kernel<D>), dim3(p.B * p.H), dim3(D), 0, st, a);

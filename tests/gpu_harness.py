@@ -89,12 +89,21 @@ def assert_quant_bit_exact(gpu: dict, qk: dict, vq: dict):
     np.testing.assert_array_equal(bits(gpu["v_mean"]), bits(vq["v_mean"]), err_msg="v means")
 
 
+def exp2_scale(d: int) -> float:
+    """sm_scale * log2(e) as the library forms it in fp32 (default sm_scale)."""
+    return float(np.float32(np.float32(1.0) / np.sqrt(np.float32(d))) * np.float32(1.4426950408889634))
+
+
 def bias_tolerance_ok(gpu_bias, ref_bias, q_mean, k_smoothed):
-    """The bias runs on bf16 matrix cores with a 3-product hi/lo split (about
-    2^-16 relative per product): |err| <= 2^-14 * sum_c |mu_c| |K'_jc| + tiny."""
-    scale = np.einsum("bhqc,bhjc->bhqj", np.abs(q_mean).astype(np.float64), np.abs(k_smoothed).astype(np.float64))
-    err = np.abs(gpu_bias.astype(np.float64) - ref_bias.astype(np.float64))
-    return np.all(err <= 2.0 ** -14 * scale + 1e-30), float((err / (scale + 1e-30)).max())
+    """The library stores dS * sm_scale * log2(e).  dS runs on bf16 matrix cores
+    with a 3-product hi/lo split (about 2^-16 relative per product):
+    |err| <= (2^-14 * sum_c |mu_c| |K'_jc| + 2^-23 |dS|) * scale."""
+    c = exp2_scale(q_mean.shape[-1])
+    mag = np.einsum("bhqc,bhjc->bhqj", np.abs(q_mean).astype(np.float64), np.abs(k_smoothed).astype(np.float64))
+    ref = ref_bias.astype(np.float64) * c
+    err = np.abs(gpu_bias.astype(np.float64) - ref)
+    bound = (2.0 ** -14 * mag + 2.0 ** -23 * np.abs(ref_bias)) * c + 1e-30
+    return np.all(err <= bound), float((err / bound).max())
 
 
 def output_tolerance(v: np.ndarray, emul: np.ndarray, dtype: str) -> np.ndarray:
