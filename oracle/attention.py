@@ -9,20 +9,28 @@ emulate_attention: the FlashAttention-style tiled online softmax the
 SageAttention2++ summary describes in "2. Preliminary" and "2.1 SageAttention2",
 on the codes produced by ``oracle.quant``:
 
-    for each 128-query block, key tiles of BK keys in ascending order
-    (tiles wholly above the diagonal are skipped when causal):
-      s   = (S_int * dQ_i * dK_j + dS_j) * sm_scale * log2(e)   (fp64 -> fp32)
-      s   = -inf for padded keys (j >= N) and, when causal, for j > i
-      m'  = max(m, max_j s);  alpha = 2^(m - m')  (0 while m = -inf)
-      P~  = 2^(s - m')                                         (fp64 -> fp32)
-      l   = alpha * l + sum_j P~
-      p^  = E4M3(P~ * P_r)        (the fixed per-block scale 1 / P_r)
-      acc = alpha * acc + sum_j dec(p^_j) * dec(v^_j)
-    O = acc * dV / (P_r * l) + mu_V, rounded once to the output dtype.
+    for each 128-query block, key steps of BK keys in ascending order
+    (steps wholly above the diagonal are skipped when causal):
+      s    = (S_int * dQ_i * dK_j + dS_j) * sm_scale * log2(e)   (fp64 -> fp32)
+      s    = -inf for padded keys (j >= N) and, when causal, for j > i
+      ms   = max_j s over the step
+      m'   = ms if ms > m + tau else m        (reference maximum, lags by <= tau)
+      alpha = 2^(m - m')                      (1 when m' = m, 0 while m = -inf)
+      P~   = 2^(s - m')  in (0, 2^tau]         (fp64 -> fp32)
+      p^   = E4M3(P~ * P_r / 2^tau)           (the fixed per-block scale)
+      l    = alpha * l + sum_j P~_j * P_r / 2^tau   (row sum of the fp32 P~)
+      acc  = alpha * acc + sum_j dec(p^_j) * dec(v^_j)
+    O = acc * dV / l + mu_V, rounded once to the output dtype.
 
+With tau = 0 this is textbook online softmax (the reference maximum is the
+running maximum).  The library's kernel uses BK = 128 and tau = 0 and sums the
+fp32 P~ (``l_fp8=False``, the plain FlashAttention reading); ``l_fp8=True``
+sums the FP8-rounded P~ instead, which makes O an exactly normalised weighted
+average of the V codes.  tau > 0 lets the reference lag the running maximum
+by up to tau (P~ <= 2^tau), which skips most O rescales.
 Everything except the fp32 values that decide an E4M3 code is float64.  The
-max is updated once per tile, so the emulated P~ depends on BK; it is a
-parameter that must equal the kernel's tile (128).
+reference maximum changes per step, so the emulated P~ depends on BK and tau;
+both must equal the kernel's.
 """
 from __future__ import annotations
 
@@ -35,6 +43,7 @@ from .quant import QBLOCK, q_group_index, k_group_index, bias_row
 
 LOG2E = 1.0 / math.log(2.0)
 DEFAULT_BK = 128
+DEFAULT_TAU = 0.0
 
 
 def _default_scale(d: int, sm_scale):
@@ -75,7 +84,8 @@ def exact_attention(q, k, v, causal=False, sm_scale=None, row_block=256):
 
 
 def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_scale=None,
-                  p_range: float = 448.0, bk: int = DEFAULT_BK, quantized: bool = True):
+                  p_range: float = 448.0, bk: int = DEFAULT_BK, quantized: bool = True,
+                  tau: float = DEFAULT_TAU, l_fp8: bool = False):
     """Emulate one 128-query block; returns (O float64 [rows, d], rows).
 
     ``quantized=False`` switches every quantiser off (identity codecs: the
@@ -97,7 +107,7 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
         dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
         vmat = e4m3_decode(vq["v_codes"][b, h])
         dv = vq["v_scale"][b, h].astype(np.float64)
-        pr = float(np.float32(p_range))
+        pscale = float(np.float32(p_range)) * 2.0 ** -tau     # E4M3 code of P~ = E4M3(P~ * pscale)
     else:
         qmat = qk["q_smoothed"][b, h, q0:q0 + QBLOCK].astype(np.float64)
         dq = np.ones(QBLOCK)
@@ -105,37 +115,39 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
         dk = np.ones(n_pad)
         vmat = vq["v_smoothed"][b, h].astype(np.float64)
         dv = np.ones(d)
-        pr = 1.0
+        pscale = 1.0
     bias = (qk["bias"][b, h, qb] if qk.get("bias") is not None else bias_row(qk, b, h, qb)).astype(np.float64)
 
     key_end = min(N, q0 + QBLOCK) if causal else N
-    n_tiles = -(-key_end // bk)
+    n_steps = -(-key_end // bk)
     m = np.full(QBLOCK, -np.inf)
     l = np.zeros(QBLOCK)
     acc = np.zeros((QBLOCK, d))
-    for t in range(n_tiles):
+    for t in range(n_steps):
         j = np.arange(t * bk, min((t + 1) * bk, n_pad))
         S = qmat @ kmat[j].T                                           # exact integers when quantized
         s = ((S * (dq[:, None] * dk[None, j]) + bias[None, j]) * scale).astype(np.float32)
         mask = (j[None, :] >= N) | (causal & (j[None, :] > qi[:, None]))
         s = np.where(mask, np.float32(-np.inf), s)
-        m_new = np.maximum(m, s.max(axis=1).astype(np.float64))
+        ms = s.max(axis=1).astype(np.float64)
+        m_new = np.where(ms > m + tau, ms, m)
         alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - np.where(np.isneginf(m_new), 0.0, m_new)))
         base = np.where(np.isneginf(m_new), 0.0, m_new)
         P = np.exp2(s.astype(np.float64) - base[:, None]).astype(np.float32)
-        l = alpha * l + P.astype(np.float64).sum(axis=1)
         if quantized:
-            pw = e4m3_decode(e4m3_encode((P * np.float32(pr)).astype(np.float32)))
+            pw = e4m3_decode(e4m3_encode((P * np.float32(pscale)).astype(np.float32)))
         else:
             pw = P.astype(np.float64)
+        l = alpha * l + (pw.sum(axis=1) if l_fp8 else P.astype(np.float64).sum(axis=1) * pscale)
         acc = alpha[:, None] * acc + pw @ vmat[j]
         m = m_new
-    o = acc * dv[None, :] / (pr * l[:, None]) + vq["v_mean"][b, h].astype(np.float64)[None, :]
+    o = acc * dv[None, :] / l[:, None] + vq["v_mean"][b, h].astype(np.float64)[None, :]
     return o[:nrows], qi[:nrows]
 
 
 def emulate_attention(qk: dict, vq: dict, causal: bool, sm_scale=None, p_range: float = 448.0,
-                      bk: int = DEFAULT_BK, quantized: bool = True, blocks=None):
+                      bk: int = DEFAULT_BK, quantized: bool = True, blocks=None,
+                      tau: float = DEFAULT_TAU, l_fp8: bool = False):
     """Emulate the whole tensor (or the (b, h, qb) triples in ``blocks``).
 
     Returns float64 [B,H,N,d] (rows of blocks not asked for are NaN).
@@ -146,7 +158,7 @@ def emulate_attention(qk: dict, vq: dict, causal: bool, sm_scale=None, p_range: 
     if blocks is None:
         blocks = [(b, h, qb) for b in range(B) for h in range(H) for qb in range(n_pad // QBLOCK)]
     for (b, h, qb) in blocks:
-        o, rows = emulate_block(qk, vq, b, h, qb, causal, sm_scale, p_range, bk, quantized)
+        o, rows = emulate_block(qk, vq, b, h, qb, causal, sm_scale, p_range, bk, quantized, tau, l_fp8)
         out[b, h, rows] = o
     return out
 

@@ -212,41 +212,66 @@ __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
                           a.out.q_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngq);
 }
 
-// Binary-counter evaluation of the pairwise tree over n leaves padded with
-// +0.0 up to the next power of two; leaves are read through `leaf(i)`.
+// Pairwise tree over the n per-block partial sums of one channel (leaves
+// padded with +0.0 up to P = 2^ceil(log2 n)), for 32 channels of one head per
+// work-group: S = min(8, P) threads per channel each reduce one aligned segment
+// of P/S leaves (8-leaf subtrees formed in registers from batched loads, then
+// merged by a binary counter kept in LDS), and the S segment sums are merged as
+// a tree in LDS.  Exactly the canonical tree, with no padding beyond P.
 template <typename F>
-__device__ __forceinline__ float tree_over_blocks(int n, F leaf) {
-  float stk[24];
-  int lvl[24];
-  int sp = 0;
+__device__ __forceinline__ float segment_tree_sum(int n, int c32, int seg, F leaf, float (*stk)[32][14],
+                                                  float (*segsum)[32]) {
   int P = 1;
   while (P < n) P <<= 1;
-  for (int i = 0; i < P; ++i) {
-    float x = i < n ? leaf(i) : 0.f;
-    int L = 0;
-    while (sp > 0 && lvl[sp - 1] == L) {
-      x = stk[sp - 1] + x;
-      --sp;
-      ++L;
+  const int S = P < 8 ? P : 8;
+  const int L = P / S;
+  float result = 0.f;
+  if (seg < S) {
+    const int first = seg * L;
+    int sp = 0, cnt = 0;
+    auto push = [&](float x) {
+      int k = cnt;
+      while (k & 1) {
+        x = stk[seg][c32][--sp] + x;
+        k >>= 1;
+      }
+      stk[seg][c32][sp++] = x;
+      ++cnt;
+    };
+    if (L >= 8) {
+      for (int i0 = 0; i0 < L; i0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = first + i0 + u;
+          v[u] = i < n ? leaf(i) : 0.f;
+        }
+        push(((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+      }
+    } else {
+      for (int i = first; i < first + L; ++i) push(i < n ? leaf(i) : 0.f);
     }
-    stk[sp] = x;
-    lvl[sp] = L;
-    ++sp;
+    result = stk[seg][c32][0];
+    segsum[seg][c32] = result;
   }
-  return stk[0];
+  __syncthreads();
+  for (int st = 1; st < S; st <<= 1) {
+    if (seg % (2 * st) == 0 && seg + st < S) segsum[seg][c32] = segsum[seg][c32] + segsum[seg + st][c32];
+    __syncthreads();
+  }
+  return segsum[0][c32];
 }
 
-// K mean from the per-block sums: one thread per channel of one head.
+// K mean: one work-group per (32-channel group, head); 256 threads = 32 channels x 8 segments.
 template <int D>
-__global__ __launch_bounds__(D) void k_mean_kernel(QKArgs a) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(256) void k_mean_kernel(QKArgs a) {
+  __shared__ float stk[8][32][14];
+  __shared__ float segsum[8][32];
+  const int bh = blockIdx.y, c = 32 * blockIdx.x + (threadIdx.x & 31), seg = threadIdx.x >> 5;
   const float* part = a.out.k_partial + static_cast<int64_t>(bh) * a.nblk * D + c;
-  float mu = 0.f;
-  if (a.smooth_k) {
-    const float sum = tree_over_blocks(a.nblk, [&](int i) { return part[static_cast<int64_t>(i) * D]; });
-    mu = sum / static_cast<float>(a.N);
-  }
-  a.out.k_mean[static_cast<int64_t>(bh) * D + c] = mu;
+  const float sum = segment_tree_sum(a.nblk, threadIdx.x & 31, seg, [&](int i) { return part[static_cast<int64_t>(i) * D]; },
+                                     stk, segsum);
+  if (seg == 0) a.out.k_mean[static_cast<int64_t>(bh) * D + c] = a.smooth_k ? sum / static_cast<float>(a.N) : 0.f;
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) {
@@ -259,83 +284,127 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 // scales, then the bias dS[qb, j] = mu_Q(qb) . K'_j for the block's keys and
 // every Q block, on the bf16 matrix cores with a three-product hi/lo split of
 // both operands (about 16 significant bits), stored times sm_scale * log2(e).
+// LDS row of D bf16 values (2D bytes): 16-byte chunk c of row r lives at chunk
+// c ^ (r & (2D/16 - 1)), so the 32 rows read together by an MFMA operand load
+// spread over the banks.
+template <int D>
+__device__ __forceinline__ int bf_off(int r, int c16) {
+  constexpr int CH = 2 * D / 16;
+  return r * 2 * D + 16 * (c16 ^ (r & (CH - 1)));
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* khi = reinterpret_cast<uint16_t*>(smem);        // [128][D]
-  uint16_t* klo = khi + 128 * D;                             // [128][D]
-  unsigned* gmax = reinterpret_cast<unsigned*>(klo + 128 * D);
+  __shared__ __attribute__((aligned(16))) uint8_t ahi[32 * 2 * D];   // [32 Q blocks][D] bf16, swizzled rows
+  __shared__ __attribute__((aligned(16))) uint8_t alo[32 * 2 * D];
+  __shared__ unsigned gmax[128];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int row0 = blk * 128;
   const int t = threadIdx.x, g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
-  float x[Tile<D>::TOK][8];
-  load_block<D, BF16>(a.k + b * a.ksB + h * a.ksH, a.ksN, row0, a.N, x);
-  const float* kmean = a.out.k_mean + static_cast<int64_t>(bh) * D + 8 * cg;
-  float mu[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) mu[e] = kmean[e];
+  const uint16_t* kin = a.k + b * a.ksB + h * a.ksH;
+  const float* kmean = a.out.k_mean + static_cast<int64_t>(bh) * D;
   const int valid = min(128, a.N - row0);
-#pragma unroll
-  for (int u = 0; u < Tile<D>::TOK; ++u) {
-    const int r = g * Tile<D>::TOK + u;
-    const bool ok = r < valid;
-    uint16_t hv[8], lv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[u][e] = ok ? x[u][e] - mu[e] : 0.f;
-      hv[e] = bf16_rne(x[u][e]);
-      lv[e] = bf16_rne(x[u][e] - __uint_as_float(static_cast<uint32_t>(hv[e]) << 16));
-    }
-    *reinterpret_cast<uint4*>(khi + r * D + 8 * cg) = *reinterpret_cast<const uint4*>(hv);
-    *reinterpret_cast<uint4*>(klo + r * D + 8 * cg) = *reinterpret_cast<const uint4*>(lv);
-  }
-  const int ngk = k_groups_per_block(a.gran);
-  quantize_block<D, false>(x, a.gran, a.qmax, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
-                           a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
-  // quantize_block passed a barrier after khi/klo were written, so they are complete here.
-
   const int w = t / 64, l = t % 64, col = l & 31, hh = l >> 5;
   const int key = 32 * w + col;
-  const float* qmean = a.out.q_mean + static_cast<int64_t>(bh) * a.nblk * D;
-  float* bias = a.out.bias + static_cast<int64_t>(bh) * a.nblk * a.n_pad + row0 + key;
-  for (int qb0 = 0; qb0 < a.nblk; qb0 += 32) {
-    f32x16 acc;
+  // Raw K rows in the MFMA operand layout, issued first so their latency
+  // overlaps the quantisation below (the second read of the block hits L2).
+  uint4 kraw[D / 16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    const int qrow = qb0 + col;
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kraw[ks] = make_uint4(0u, 0u, 0u, 0u);
+    if (key < valid) kraw[ks] = *reinterpret_cast<const uint4*>(kin + static_cast<int64_t>(row0 + key) * a.ksN + 16 * ks + 8 * hh);
+  }
+  {
+    float x[Tile<D>::TOK][8];
+    load_block<D, BF16>(kin, a.ksN, row0, a.N, x);
+    float mu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mu[e] = kmean[8 * cg + e];
+#pragma unroll
+    for (int u = 0; u < Tile<D>::TOK; ++u) {
+      const bool ok = g * Tile<D>::TOK + u < valid;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[u][e] = ok ? x[u][e] - mu[e] : 0.f;
+    }
+    const int ngk = k_groups_per_block(a.gran);
+    quantize_block<D, false>(x, a.gran, a.qmax, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+                             a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
+  }
+
+  bf16x8 Bhi[D / 16], Blo[D / 16];
+  {
+    const bool ok = key < valid;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int c0 = 16 * ks + 8 * hh;
-      float mv[8];
-      if (qrow < a.nblk) {
-        const float4 m0 = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qrow) * D + c0);
-        const float4 m1 = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qrow) * D + c0 + 4);
-        mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
-        mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
-      } else {
+      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&kraw[ks]);
+      uint16_t bh16[8], bl16[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mv[e] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const float kp = ok ? to_f32<BF16>(hv[e]) - kmean[c0 + e] : 0.f;
+        bh16[e] = bf16_rne(kp);
+        bl16[e] = bf16_rne(kp - __uint_as_float(static_cast<uint32_t>(bh16[e]) << 16));
       }
+      Bhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bh16));
+      Blo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bl16));
+    }
+  }
+  const float* qmean = a.out.q_mean + static_cast<int64_t>(bh) * a.nblk * D;
+  float* bias = a.out.bias + static_cast<int64_t>(bh) * a.nblk * a.n_pad + row0 + key;
+  constexpr int APT = 32 * D / 8 / kThreads;    // 8-channel pieces of the mu_Q tile per thread
+  float4 mq[APT][2];
+  auto fetch_mu = [&](int qb0) {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const int piece = t + kThreads * i;
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      mq[i][0] = mq[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qb0 + row < a.nblk) {
+        mq[i][0] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qb0 + row) * D + 8 * c8);
+        mq[i][1] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qb0 + row) * D + 8 * c8 + 4);
+      }
+    }
+  };
+  fetch_mu(0);
+  for (int qb0 = 0; qb0 < a.nblk; qb0 += 32) {
+    // The 32 x D mu_Q tile, split into bf16 hi/lo once for all four waves;
+    // the next tile's values are fetched while this one is used.
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const int piece = t + kThreads * i;
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      const float mv[8] = {mq[i][0].x, mq[i][0].y, mq[i][0].z, mq[i][0].w,
+                           mq[i][1].x, mq[i][1].y, mq[i][1].z, mq[i][1].w};
       uint16_t ah[8], al[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ah[e] = bf16_rne(mv[e]);
         al[e] = bf16_rne(mv[e] - __uint_as_float(static_cast<uint32_t>(ah[e]) << 16));
       }
-      const bf16x8 A_hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ah));
-      const bf16x8 A_lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(al));
-      const bf16x8 B_hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(khi + key * D + c0));
-      const bf16x8 B_lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(klo + key * D + c0));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, B_hi, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, B_lo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_lo, B_hi, acc, 0, 0, 0);
+      *reinterpret_cast<uint4*>(ahi + bf_off<D>(row, c8)) = *reinterpret_cast<const uint4*>(ah);
+      *reinterpret_cast<uint4*>(alo + bf_off<D>(row, c8)) = *reinterpret_cast<const uint4*>(al);
+    }
+    if (qb0 + 32 < a.nblk) fetch_mu(qb0 + 32);
+    __syncthreads();
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int c16 = 2 * ks + hh;
+      const bf16x8 A_hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ahi + bf_off<D>(col, c16)));
+      const bf16x8 A_lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(alo + bf_off<D>(col, c16)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Bhi[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Blo[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_lo, Bhi[ks], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int qb = qb0 + 8 * (i >> 2) + 4 * hh + (i & 3);
       if (qb < a.nblk) bias[static_cast<int64_t>(qb) * a.n_pad] = acc[i] * a.scale_log2;
     }
+    __syncthreads();   // the next tile overwrites ahi/alo
   }
 }
 
@@ -403,27 +472,37 @@ __global__ __launch_bounds__(kThreads) void v_stats_kernel(VArgs a) {
   }
 }
 
-// V pass 2: mean, amax, scale and reciprocal scale per channel of one head.
-// The reciprocal is parked in block 0's sum slot (only this thread reads it).
+// V pass 2: mean, amax, scale and reciprocal scale per channel, one
+// work-group per (32-channel group, head).  The reciprocal scale is parked in
+// block 0's sum slot, which only this work-group reads (before the write).
 template <int D>
-__global__ __launch_bounds__(D) void v_finalize_kernel(VArgs a) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(256) void v_finalize_kernel(VArgs a) {
+  __shared__ float stk[8][32][14];
+  __shared__ float segsum[8][32];
+  __shared__ float mx[8][32], mn[8][32];
+  const int bh = blockIdx.y, c32 = threadIdx.x & 31, c = 32 * blockIdx.x + c32, seg = threadIdx.x >> 5;
   float* part = a.out.v_partial + static_cast<int64_t>(bh) * a.nblk * 3 * D;
-  float mu = 0.f;
-  if (a.smooth_v) {
-    const float sum = tree_over_blocks(a.nblk, [&](int i) { return part[static_cast<int64_t>(i) * 3 * D + c]; });
-    mu = sum / static_cast<float>(a.N);
-  }
   float vmax = -INFINITY, vmin = INFINITY;
-  for (int i = 0; i < a.nblk; ++i) {
+  for (int i = seg; i < a.nblk; i += 8) {
     vmax = fmaxf(vmax, part[static_cast<int64_t>(i) * 3 * D + D + c]);
     vmin = fminf(vmin, part[static_cast<int64_t>(i) * 3 * D + 2 * D + c]);
   }
-  // max_n |fl(V_n - mu)| = max(fl(vmax - mu), fl(mu - vmin)): fl(x - mu) is monotone in x.
-  const float amax = fmaxf(vmax - mu, mu - vmin);
-  a.out.v_scale[static_cast<int64_t>(bh) * D + c] = amax / a.v_range;
-  a.out.v_mean[static_cast<int64_t>(bh) * D + c] = mu;
-  part[c] = amax > 0.f ? a.v_range / amax : 0.f;
+  mx[seg][c32] = vmax;
+  mn[seg][c32] = vmin;
+  const float sum = segment_tree_sum(a.nblk, c32, seg, [&](int i) { return part[static_cast<int64_t>(i) * 3 * D + c]; },
+                                     stk, segsum);   // its barriers publish mx, mn
+  if (seg == 0) {
+    for (int s2 = 1; s2 < 8; ++s2) {
+      vmax = fmaxf(vmax, mx[s2][c32]);
+      vmin = fminf(vmin, mn[s2][c32]);
+    }
+    const float mu = a.smooth_v ? sum / static_cast<float>(a.N) : 0.f;
+    // max_n |fl(V_n - mu)| = max(fl(vmax - mu), fl(mu - vmin)): fl(x - mu) is monotone in x.
+    const float amax = fmaxf(vmax - mu, mu - vmin);
+    a.out.v_scale[static_cast<int64_t>(bh) * D + c] = amax / a.v_range;
+    a.out.v_mean[static_cast<int64_t>(bh) * D + c] = mu;
+    part[c] = amax > 0.f ? a.v_range / amax : 0.f;
+  }
 }
 
 // Position of key r (0..127 inside a 128-key block) in the permuted V layout.
@@ -453,18 +532,23 @@ __global__ __launch_bounds__(kThreads) void v_encode_kernel(VArgs a) {
     inv[e] = part[8 * cg + e];
   }
   const int valid = min(128, a.N - row0);
+  // Four consecutive tokens 4k..4k+3 of one channel sit at four consecutive
+  // permuted positions, so they are converted as two token pairs and written
+  // as one 32-bit word.
 #pragma unroll
-  for (int u = 0; u < Tile<D>::TOK; ++u) {
-    const int r = g * Tile<D>::TOK + u;
-    const bool ok = r < valid;
+  for (int u4 = 0; u4 < Tile<D>::TOK; u4 += 4) {
+    const int r = g * Tile<D>::TOK + u4;
     const int pos = v_perm(r);
+    float pv[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = (x[u][e] - mu[e]) * inv[e];
-      const float p1 = (x[u][e + 1] - mu[e + 1]) * inv[e + 1];
-      const int pk = ok ? __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false) : 0;
-      tile[(8 * cg + e) * 128 + pos] = static_cast<uint8_t>(pk & 0xff);
-      tile[(8 * cg + e + 1) * 128 + pos] = static_cast<uint8_t>((pk >> 8) & 0xff);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[j][e] = r + j < valid ? (x[u4 + j][e] - mu[e]) * inv[e] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0][e], pv[1][e], 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2][e], pv[3][e], wd, true);
+      *reinterpret_cast<int*>(tile + (8 * cg + e) * 128 + pos) = wd;
     }
   }
   __syncthreads();
@@ -491,16 +575,8 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
   hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((k_mean_kernel<D>), dim3(p.B * p.H), dim3(D), 0, st, a);
-  const size_t smem = 2 * 128 * D * sizeof(uint16_t) + 128 * sizeof(unsigned);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_quant_bias_kernel<D, BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16>), grid, dim3(kThreads), smem, st, a);
+  hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -514,7 +590,7 @@ hipError_t quant_v_impl(const Problem& p, TensorView v, const sage_v_buffers& ou
   a.v_range = p.v_range;
   const dim3 grid(p.nblk, p.B * p.H);
   hipLaunchKernelGGL((v_stats_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((v_finalize_kernel<D>), dim3(p.B * p.H), dim3(D), 0, st, a);
+  hipLaunchKernelGGL((v_finalize_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
   hipLaunchKernelGGL((v_encode_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -61,6 +61,8 @@ SMALL = {
     "n127": ("tiny", dict(N=127)),
     "n129_causal": ("tiny", dict(N=129, causal=True)),
     "n255_d128": ("target", dict(H=1, N=255)),
+    "one_head_n9000": ("target", dict(H=1, N=9000)),            # 71 blocks: batched finalize path
+    "one_head_n9000_causal_int4": ("long_context_int4", dict(H=1, N=9000)),
 }
 
 
