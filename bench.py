@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0      # MI355X dense INT8 and FP8 matrix peak (both 5.0 P/s)
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 30    # calibration copy: reads and writes this many bytes
 COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_counters.json")
 
 
@@ -49,7 +50,7 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, sample_blocks: int = 24):
+def cpu_baseline(w, sample_blocks: int = 96):
     """Time the oracle on one head: quantisation of the head plus the tiled
     emulation of `sample_blocks` query blocks, extrapolated to the workload."""
     import numpy as np
@@ -97,6 +98,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run 3 plain 1 GiB device-to-device elementwise copies (neg) whose "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figure")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -150,6 +154,14 @@ def main():
     qk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     v_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     tops = w.ops / (ms_per_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_ms * 1e-3) / 1e12

@@ -185,3 +185,40 @@ def test_planted_wrong_k_group_map_degrades_accuracy(monkeypatch):
     monkeypatch.setattr(oa, "k_group_index", lambda n, g: real(n, g) ^ 1)   # swap the two halves
     bad = oracle.compare(ex, oracle.emulate_attention(qk, vq, False))["rmse"]
     assert bad > 1.5 * good
+
+
+# Plausible slips in the online-softmax bookkeeping, planted into a copy of
+# the oracle's block routine by source substitution; the identity-codec check
+# against exact attention must catch every one.
+MUTATIONS = {
+    "no O rescale": ("acc = alpha[:, None] * acc + pw @ vmat[j]", "acc = acc + pw @ vmat[j]"),
+    "no l rescale": ("l = alpha * l + ", "l = l + "),
+    "causal off by one": ("(j[None, :] > qi[:, None])", "(j[None, :] >= qi[:, None])"),
+    "padded keys kept": ("(j[None, :] >= N) |", "(j[None, :] >= n_pad) |"),
+    "alpha inverted": ("np.exp2(m - np.where", "np.exp2(-m + 2 * m - 2 * m + np.where"),
+    "V mean dropped": ("+ vq[\"v_mean\"][b, h].astype(np.float64)[None, :]", "+ 0.0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_softmax_bookkeeping_slips_are_caught(name, monkeypatch):
+    import inspect
+    import textwrap
+    import oracle.attention as oa
+    old, new = MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(oa.emulate_block))
+    assert src.count(old) == 1, f"mutation anchor for {name!r} not found once"
+    ns = dict(vars(oa))
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    monkeypatch.setattr(oa, "emulate_block", ns["emulate_block"])
+    w = scaled(WORKLOADS["image_dit"], B=1, H=1, N=300)   # V with channel means; ragged tail
+    q, k, v = make_inputs(w)
+    qk, vq = oracle.quant_qk(q, k), oracle.quant_v(v)
+    for causal in (True, False):
+        ex = oracle.exact_attention(q, k, v, causal)
+        for tau in (0.0, 2.0):
+            with np.errstate(all="ignore"):
+                em = oa.emulate_attention(qk, vq, causal, quantized=False, tau=tau)
+            if not np.abs(em - ex).max() <= 1e-3:      # NaN counts as caught
+                return
+    raise AssertionError(f"planted slip {name!r} went unnoticed")

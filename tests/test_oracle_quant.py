@@ -2,11 +2,13 @@
 import json
 import math
 import os
+import sys
 
 import numpy as np
 import pytest
 
 import oracle
+import oracle.quant as oq
 from oracle.fp8 import e4m3_decode
 from oracle.quant import QuantParams, quantize_rows, k_group_index, q_group_index, bias_row, n_padded
 from oracle.reduce import canonical_sum, canonical_mean, pad_length
@@ -191,3 +193,37 @@ def test_generators_are_deterministic_and_padded_sizes():
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     assert n_padded(300) == 384 and n_padded(32760) == 32768
+
+
+# Plausible slips in the integer quantiser, planted into a copy of the
+# oracle's routine by source substitution: the hand-worked examples or the
+# invariants above must catch each one.
+QUANT_MUTATIONS = {
+    "floor instead of rint": ("np.rint(prod)", "np.floor(prod)"),
+    "amax without abs": ("np.abs(xs).max(axis=-1)", "xs.max(axis=-1)"),
+    "scale off by one": ("delta = (amax / qm)", "delta = (amax / (qm + 1))"),
+    "no clamp": ("np.clip(np.rint(prod), -qmax, qmax)", "np.rint(prod * np.float32(1.0001))"),
+    "row amax instead of group amax": ("inv_rows = inv[..., groups]",
+                                       "inv_rows = np.where(row_amax > 0, qm / np.maximum(row_amax, 1e-30), 0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTATIONS))
+def test_planted_quantiser_slips_are_caught(name, monkeypatch):
+    import inspect
+    import textwrap
+    old, new = QUANT_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(oq.quantize_rows))
+    assert src.count(old) == 1, f"mutation anchor for {name!r} not found once"
+    ns = dict(vars(oq))
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    monkeypatch.setattr(oq, "quantize_rows", ns["quantize_rows"])
+    monkeypatch.setattr(sys.modules[__name__], "quantize_rows", ns["quantize_rows"])
+    caught = 0
+    for check in (test_quantiser_hand_examples, lambda: test_quantiser_invariants("thread", 8)):
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except (AssertionError, ValueError, OverflowError):
+            caught += 1
+    assert caught, f"planted slip {name!r} went unnoticed"
