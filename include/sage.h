@@ -12,8 +12,12 @@
  *   Q', K'  -> integer codes with per-group scales (INT8, or INT4-range [-7,7]
  *              held in int8 and run on the INT8 matrix cores)
  *   V'  = V - mean_tokens(V); V' -> FP8 E4M3 with per-channel scales
- *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles;
- *   P~  -> FP8 E4M3 with the fixed scale 1/P_r;  O = sum P~ V' / l + mean(V).
+ *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles against a
+ *         reference maximum m that moves only when a tile's row maximum exceeds
+ *         it by more than 4 (log2 units), so P~ = 2^(s - m) <= 16 with s the
+ *         score in log2 units (S sm_scale log2 e);
+ *   P~  -> FP8 E4M3 with the fixed scale P_r / 16;  O = sum P~ V' / l + mean(V),
+ *         l = sum of the fp32 P~.
  *
  * All entry points are plain C with device pointers, sizes and a HIP stream
  * (passed as void*, a hipStream_t; NULL is the default stream).  The library
@@ -81,7 +85,7 @@ typedef struct {
   int32_t smooth_q;  /* 1 (default): subtract the 128-token block mean of Q   */
   int32_t smooth_k;  /* 1 (default): subtract the token mean of K             */
   int32_t smooth_v;  /* 1 (default): subtract the token mean of V             */
-  float p_range;     /* P_r in (0, 448], default 448: P~ code = E4M3(P~ * P_r) */
+  float p_range;     /* P_r in (0, 448], default 448: P~ code = E4M3(P~ * P_r / 16) */
   float v_range;     /* V_r in (0, 448], default 448: V code = E4M3(V' V_r/amax) */
   float sm_scale;    /* softmax scale; 0 (default) means 1/sqrt(d)            */
 } sage_params;

@@ -23,11 +23,11 @@ on the codes produced by ``oracle.quant``:
     O = acc * dV / l + mu_V, rounded once to the output dtype.
 
 With tau = 0 this is textbook online softmax (the reference maximum is the
-running maximum).  The library's kernel uses BK = 128 and tau = 0 and sums the
-fp32 P~ (``l_fp8=False``, the plain FlashAttention reading); ``l_fp8=True``
-sums the FP8-rounded P~ instead, which makes O an exactly normalised weighted
-average of the V codes.  tau > 0 lets the reference lag the running maximum
-by up to tau (P~ <= 2^tau), which skips most O rescales.
+running maximum).  tau > 0 lets the reference lag the running maximum by up
+to tau (P~ <= 2^tau), which skips most O rescales.  The library's kernel uses
+BK = 128 and tau = 4 and sums the fp32 P~ (``l_fp8=False``, the plain
+FlashAttention reading); ``l_fp8=True`` sums the FP8-rounded P~ instead,
+which makes O an exactly normalised weighted average of the V codes.
 Everything except the fp32 values that decide an E4M3 code is float64.  The
 reference maximum changes per step, so the emulated P~ depends on BK and tau;
 both must equal the kernel's.
@@ -43,7 +43,7 @@ from .quant import QBLOCK, q_group_index, k_group_index, bias_row
 
 LOG2E = 1.0 / math.log(2.0)
 DEFAULT_BK = 128
-DEFAULT_TAU = 0.0
+DEFAULT_TAU = 4.0
 
 
 def _default_scale(d: int, sm_scale):

@@ -3,23 +3,32 @@
 // Method: the FlashAttention-based quantized attention of the SageAttention2++
 // summary ("2. Preliminary", "2.1 SageAttention2"): INT8 (or INT4-range)
 // Q, K codes with per-group scales, dequantised S plus the Q-smoothing bias,
-// online softmax, P~ to FP8 with the fixed scale 1/P_r, FP8 V with per-channel
+// online softmax, P~ to FP8 with a fixed scale, FP8 V with per-channel
 // scales, rescale and normalise at the end.
 //
 // Mapping to the hardware:
-//  * one work-group of 4 waves per 128-query block; wave w owns 32 queries.
+//  * one work-group of 4 waves per 128-query block; wave w owns 32 queries;
+//    keys advance in tiles of 128.
 //  * S^T = K^ Q^T on v_mfma_i32_32x32x32_i8: the A operand is 32 keys x 32
 //    channels of K^ (from LDS), the B operand 32 channels x 32 queries of Q^
 //    (registers for the whole kernel).  In the 32x32 accumulator lane l holds
 //    query l%32 and the 16 keys 8a + 4(l/32) + b, so row max and row sum are
 //    in-lane work plus one exchange with lane l^32.
-//  * the 16 fp8-packed P~ values of two consecutive 32-key S tiles are
+//  * the 16 fp8-packed P~ values of two consecutive 32-key S subtiles are
 //    exactly one lane's 32-byte B operand of v_mfma_f32_32x32x64_f8f6f4
 //    (O^T += V^T P~^T, keys as the reduction index).  The V codes are stored
 //    channel-major with the matching in-group key order, so P~ never leaves
 //    registers.
-//  * one online-softmax update per 128-key tile; exp2 on v_exp_f32 with the
-//    log2(e) softmax scale and log2(P_r) folded into the exponent.
+//  * a single wave issues vector instructions only every few cycles, so its
+//    matrix-core work is interleaved with its own vector work: tile t's
+//    dequantisation and row maximum run beside the PV product of tile t-1,
+//    and tile t's exp2 / FP8 packing beside the QK product of tile t+1.
+//  * online softmax against a reference maximum that may lag the running
+//    maximum by up to TAU (log2 units): the reference moves, and O is
+//    rescaled, only when a tile's maximum exceeds it by more than TAU.  P~ is
+//    then at most 2^TAU and is encoded as E4M3(P~ * P_r / 2^TAU).
+//  * K codes, V codes and each tile's bias row and K scales are copied straight
+//    from global memory into two-slot LDS rings, one tile ahead of their use.
 #include "sage_internal.h"
 
 namespace sage {
@@ -29,6 +38,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 128;        // keys per tile (one online-softmax update)
+constexpr float kTau = 4.0f;      // allowed lag of the reference maximum (log2 units)
 
 struct AttnArgs {
   const int8_t* q_codes;
@@ -47,7 +59,7 @@ struct AttnArgs {
 };
 
 // 16-byte chunk swizzle inside a tile row so that the 16 lanes served together
-// by one ds_read_b128 pass touch distinct banks.
+// by one ds_read_b128 pass touch distinct banks (self-inverse in `chunk`).
 template <int ROW_BYTES>
 __device__ __forceinline__ int swz(int row, int chunk) {
   constexpr int CPR = ROW_BYTES / 16;
@@ -78,24 +90,52 @@ __device__ __forceinline__ void map_block(int id, int total, int nblk, int causa
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(void* p) { return (lds_void*)(p); }
 
+// LDS rings of two slots; tile u lives in slot u % 2.  K slot: 128 keys x D
+// codes (rows swizzled).  V slot: D channels x 128 keys (rows swizzled).  Aux
+// slot: the tile's 128 bias values, then its K scales (8 or 2 used).
 template <int D>
-struct TileBuf {
-  static constexpr int K_BYTES = 128 * D;          // K codes, 128 keys x D, rows swizzled
-  static constexpr int V_BYTES = D * 128;          // V codes, D channels x 128 keys, rows swizzled
-  static constexpr int B_BYTES = 128 * 4;          // bias of the 128 keys
-  static constexpr int S_BYTES = 64 * 4;           // K scales of the tile (8 or 2 used)
-  static constexpr int BYTES = K_BYTES + V_BYTES + B_BYTES + S_BYTES;
+struct Rings {
+  static constexpr int K = kTile * D;
+  static constexpr int V = D * kTile;
+  static constexpr int AUX = 1024;   // bias (512 B), K scales, spare row at 768
+  static constexpr int K0 = 0, V0 = 2 * K, A0 = 2 * K + 2 * V;
+  static constexpr int BYTES = 2 * (K + V + AUX);
+  static constexpr int J = D / 32;   // 1 KiB copies per wave for one K or V slot
 };
 
-// Direct global->LDS copies of one key tile through buffer resources (raw
-// buffers: reads past num_records return zero instead of faulting).  Lane L of
-// a wave-wide copy always lands at (LDS base + 16 L), so each lane fetches the
-// chunk that belongs at its destination in the swizzled layout.  With chunk
-// p = 256 j + threadIdx.x, the swizzled column does not depend on j, so one
-// per-lane offset serves every copy of a stream and j moves only the scalar
-// offset (4096 j bytes of K rows, 32 j channel rows of V).
+// Buffer resource (raw, 32-bit data format) over `bytes` bytes at p, in SGPRs.
+// Reads past the end return zero.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct global->LDS copies (buffer_load ... lds): lane L's 16 (or 4) bytes
+// land at M0 + 16 L (4 L).  Written as inline assembly so that the compiler
+// does not track these LDS writes: the slots a tile reads are never the ones
+// being filled (the ring schedule and the barriers guarantee it), and the
+// copies are waited for by hand (s_waitcnt vmcnt) before the barrier that
+// publishes them.  The "memory" clobber keeps LDS reads on their side.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+}
+
+// Sources of the tile copies.  With chunk p = 256 j + threadIdx.x the swizzled
+// column does not depend on j, so one per-lane offset per stream serves every
+// copy and j moves only the scalar offset (4096 j bytes of K rows, 32 j
+// channel rows of V).
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t k, v, b, s;
+  i32x4 k, v, b, s;
   uint32_t k_off, v_off, b_off;   // per-lane byte offsets for j = 0 and k0 = 0
   uint32_t v_row;                 // bytes per V channel row (n_pad)
   uint32_t s_per_tile;            // K scale groups per 128-key tile (8 or 2)
@@ -106,12 +146,11 @@ __device__ __forceinline__ TileSrc make_tile_src(const int8_t* kbase, const uint
                                                  const float* kscale, int n_scale, int n_pad, int t) {
   constexpr int CPR = D / 16;
   TileSrc s;
-  const uint32_t flags = 0x00020000u;   // raw 32-bit data format, no swizzle
-  s.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kbase), 0, n_pad * D, flags);
-  s.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase), 0, n_pad * D, flags);
-  s.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(brow), 0, n_pad * 4, flags);
-  s.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kscale), 0, n_scale * 4, flags);
-  s.s_per_tile = static_cast<uint32_t>(n_scale / (n_pad / 128));
+  s.k = buffer_rsrc(kbase, static_cast<uint32_t>(n_pad * D));
+  s.v = buffer_rsrc(vbase, static_cast<uint32_t>(n_pad * D));
+  s.b = buffer_rsrc(brow, static_cast<uint32_t>(n_pad * 4));
+  s.s = buffer_rsrc(kscale, static_cast<uint32_t>(n_scale * 4));
+  s.s_per_tile = static_cast<uint32_t>(n_scale / (n_pad / kTile));
   const int r = t / CPR, pc = t % CPR;
   s.k_off = static_cast<uint32_t>(r * D + 16 * swz<D>(r, pc));
   const int ch = t >> 3, vc = t & 7;
@@ -121,36 +160,47 @@ __device__ __forceinline__ TileSrc make_tile_src(const int8_t* kbase, const uint
   return s;
 }
 
+// K codes of the 128 keys from k0 into the K slot at LDS address `slot`.
 template <int D>
-__device__ __forceinline__ void issue_tile(uint8_t* buf, const TileSrc& s, int k0, int w) {
+__device__ __forceinline__ void copy_k(uint32_t slot, const TileSrc& s, int k0, int w) {
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.k, lds_ptr(buf + (4 * j + w) * 1024), 16, s.k_off,
-                                             static_cast<uint32_t>(k0 * D + 4096 * j), 0, 0);
-  uint8_t* vb = buf + TileBuf<D>::K_BYTES;
+  for (int j = 0; j < Rings<D>::J; ++j)
+    dma16(s.k, s.k_off, static_cast<uint32_t>(k0 * D + 4096 * j), slot + (4 * j + w) * 1024);
+}
+
+// V codes of the 128 keys from k0 (all D channels) into a V slot.
+template <int D>
+__device__ __forceinline__ void copy_v(uint32_t slot, const TileSrc& s, int k0, int w) {
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.v, lds_ptr(vb + (4 * j + w) * 1024), 16, s.v_off,
-                                             static_cast<uint32_t>(k0) + 32u * j * s.v_row, 0, 0);
-  if (w < 2) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.b, lds_ptr(buf + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES + 256 * w),
-                                             4, s.b_off, static_cast<uint32_t>(4 * k0), 0, 0);
-  } else if (w == 2 && s.b_off - 512u < 4u * s.s_per_tile) {
-    // lanes 0 .. s_per_tile-1 of wave 2 copy the tile's K scales (lane l reads scale l)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        s.s, lds_ptr(buf + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES + TileBuf<D>::B_BYTES), 4, s.b_off - 512u,
-        static_cast<uint32_t>(4 * (k0 / 128) * s.s_per_tile), 0, 0);
+  for (int j = 0; j < Rings<D>::J; ++j)
+    dma16(s.v, s.v_off, static_cast<uint32_t>(k0) + 32u * j * s.v_row, slot + (4 * j + w) * 1024);
+}
+
+// Bias row (waves 0, 1), K scales (wave 2, lanes below s_per_tile) of the 128
+// keys from k0 into an aux slot; wave 3 copies the bias again into a spare row
+// so that every wave issues exactly one copy.
+__device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, int k0, int w) {
+  if (w != 2) {
+    dma4(s.b, w == 3 ? (s.b_off & 255u) : s.b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
+  } else {
+    const uint32_t lane4 = s.b_off - 512u;
+    dma4(s.s, lane4 < 4u * s.s_per_tile ? lane4 : 0u, static_cast<uint32_t>(4 * (k0 / kTile) * s.s_per_tile),
+         slot + 512);
   }
 }
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;  // 32-channel k-steps of the QK product
-  constexpr int CT = D / 32;  // 32-channel tiles of the output
-  // Two distinct LDS objects (not halves of one array) so the compiler can see
-  // that reads of the current tile do not alias the copies into the other.
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[TileBuf<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[TileBuf<D>::BYTES];
+  constexpr int KS = D / 32;          // 32-channel k-steps of the QK product
+  constexpr int CT = D / 32;          // 32-channel tiles of the output
+  constexpr int NQK = 4 * KS;         // QK MFMAs per tile
+  constexpr int NPV = 2 * CT;         // PV MFMAs per tile
+  constexpr int QK_EVERY = 16 / NQK;  // softmax quads per QK MFMA
+  constexpr int PV_EVERY = 16 / NPV;  // dequant quads per PV MFMA
+  constexpr int J = Rings<D>::J;
+  using R = Rings<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[R::BYTES];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_ptr(lds)));
 
   const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, held in a scalar register
@@ -160,14 +210,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int qi = q0 + 32 * w + col;
 
   const int key_end = a.causal ? min(a.N, q0 + 128) : a.N;
-  const int ntiles = (key_end + 127) / 128;
+  const int ntiles = (key_end + kTile - 1) / kTile;
   const int8_t* kbase = a.k_codes + static_cast<int64_t>(bh) * a.n_pad * D;
   const uint8_t* vbase = a.v_codes + static_cast<int64_t>(bh) * D * a.n_pad;
   const float* brow = a.bias + (static_cast<int64_t>(bh) * a.nblk + qb) * a.n_pad;
   const int n_kscale = a.gran == SAGE_GRAN_THREAD ? a.n_pad / 16 : a.n_pad / 64;
   const float* kscale = a.k_scale + static_cast<int64_t>(bh) * n_kscale;
-  const TileSrc src = make_tile_src<D>(kbase, vbase, brow, kscale, n_kscale, a.n_pad, t);
-  issue_tile<D>(buf0, src, 0, w);
 
   i32x4 qf[KS];
   {
@@ -184,6 +232,60 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     dq = a.q_scale[static_cast<int64_t>(bh) * a.nblk + qb];
   }
   const float dq2 = dq * a.scale_log2;
+  // exp2(x - (m + base_shift)) = P~ * P_r / 2^TAU with P~ = exp2(x - m)
+  const float base_shift = kTau - a.log2_pr;
+  const bool thread_gran = a.gran == SAGE_GRAN_THREAD;
+
+  // First key of tile u; tiles past the end copy the last tile again (their
+  // data is never used, and every wave keeps one copy count per issue point).
+  auto kofs = [&](int u) __attribute__((always_inline)) { return min(u, ntiles - 1) * kTile; };
+
+  const TileSrc src = make_tile_src<D>(kbase, vbase, brow, kscale, n_kscale, a.n_pad, t);
+  // Tile t reads K of tile t+1 (and t's own K only in the prologue), V of tile
+  // t-1 and the aux row of tile t.  It copies K of tile t+2 and the aux row of
+  // tile t+1 when it starts, and V of tile t+1 once every wave has read V of
+  // tile t-1 (mid-tile).  Tile 0's PV product reads the V slot of tile -1,
+  // zero-filled here (its P~ is 0 too).
+  copy_k<D>(lds0 + R::K0, src, kofs(0), w);
+  copy_aux(lds0 + R::A0, src, kofs(0), w);
+  copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
+  copy_v<D>(lds0 + R::V0, src, kofs(0), w);
+  {
+    uint4* vz = reinterpret_cast<uint4*>(lds + R::V0 + R::V);
+#pragma unroll
+    for (int i = t; i < R::V / 16; i += 256) vz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // Per-lane byte offsets of the LDS fragments, relative to a slot.  The
+  // swizzle term does not depend on the subtile (K) or the channel tile (V),
+  // so those move only the immediate offset of the read.
+  //   K fragment, subtile st, channels 32kk..: kofl[kk] + 32 st D
+  //   V fragment, keys 64kc.. (lane's 32), channels 32c..: vofl[kc][h2] + 32 c kTile, h2 = 0, 1
+  //   bias quad (subtile st, a): 16 hh + 4 (32 st + 8 a)
+  uint32_t kofl[KS], vofl[2][2];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) kofl[kk] = static_cast<uint32_t>(col * D + 16 * swz<D>(col, 2 * kk + hh));
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      vofl[kc][h2] = static_cast<uint32_t>(col * kTile + 16 * swz<128>(col, 4 * kc + 2 * hh + h2));
+
+  auto lds_i4 = [&](uint32_t off) __attribute__((always_inline)) {
+    return *reinterpret_cast<const i32x4*>(lds + off);
+  };
+  auto k_frag = [&](const uint32_t* ko, int slot_off, int st, int kk) __attribute__((always_inline)) {
+    return lds_i4(ko[kk] + slot_off + 32 * st * D);
+  };
+  auto v_frag = [&](const uint32_t (*vo)[2], int slot_off, int kc, int c) __attribute__((always_inline)) {
+    const i32x4 v0 = lds_i4(vo[kc][0] + slot_off + 32 * c * kTile);
+    const i32x4 v1 = lds_i4(vo[kc][1] + slot_off + 32 * c * kTile);
+    i32x8 va;
+    va[0] = v0[0]; va[1] = v0[1]; va[2] = v0[2]; va[3] = v0[3];
+    va[4] = v1[0]; va[5] = v1[1]; va[6] = v1[2]; va[7] = v1[3];
+    return va;
+  };
 
   f32x16 oacc[CT];
 #pragma unroll
@@ -191,113 +293,192 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
+  i32x16 sA[4], sB[4];     // S^T of the tile whose softmax runs next (alternating sets)
+  i32x8 pA[2], pB[2];      // FP8 P~ of the previous tile (alternating sets)
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pA[kc][i] = 0;
 
-  auto step = [&](const int tt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-    const int k0 = tt * 128;
-    // This thread's copies of tile tt are complete; after the barrier everyone's
-    // are, and every wave has finished reading `nxt` (it held tile tt-1).
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tt + 1 < ntiles) issue_tile<D>(nxt, src, k0 + 128, w);
+  // QK product of tile 0 (not overlapped).
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sA[st][i] = 0;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      sA[st] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k_frag(kofl, R::K0, st, kk), qf[kk], sA[st], 0, 0, 0);
+  }
 
-    const int8_t* ks = reinterpret_cast<const int8_t*>(cur);
-    const uint8_t* vs = cur + TileBuf<D>::K_BYTES;
-    const float* bs = reinterpret_cast<const float*>(cur + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES);
-    const float* ksc = reinterpret_cast<const float*>(cur + TileBuf<D>::K_BYTES + TileBuf<D>::V_BYTES +
-                                                      TileBuf<D>::B_BYTES);
+  // One tile.  CUR: its ring slot (t % 2); S_cur / S_nxt: S^T of tiles t and
+  // t+1; pb_prv / pb_cur: FP8 P~ of tiles t-1 and t.
+  auto tile = [&](const int tt, auto cur_slot, i32x16* S_cur, i32x16* S_nxt, i32x8* pb_prv, i32x8* pb_cur)
+                  __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_slot)::value, NXT = 1 - CUR;
+    const int k0 = tt * kTile;
+    // This wave's copies of aux(t) (issued when tile t-1 started) and of V(t)
+    // are complete; only the 2J copies of K(t+1) and V(t) issued in phase B of
+    // tile t-1... (see the mid-tile wait) may still run.  After the barrier
+    // every wave is done with aux(t-1), whose slot is refilled below.
+    if constexpr (J == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    copy_aux(lds0 + R::A0 + NXT * R::AUX, src, kofs(tt + 1), w);
+
+    // Fresh copies of the lane offsets: without this the compiler hoists one
+    // address register per (slot, fragment) out of the loop and spills them.
+    uint32_t ko[KS], vo[2][2], bo = 16u * hh;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) { ko[kk] = kofl[kk]; asm volatile("" : "+v"(ko[kk])); }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      vo[kc][0] = vofl[kc][0]; vo[kc][1] = vofl[kc][1];
+      asm volatile("" : "+v"(vo[kc][0]), "+v"(vo[kc][1]));
+    }
+    asm volatile("" : "+v"(bo));
+    const int aux = R::A0 + CUR * R::AUX;
     float cs[4];
+    {
+      const float* ksc = reinterpret_cast<const float*>(lds + aux + 512);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) cs[st] = dq2 * (a.gran == SAGE_GRAN_THREAD ? ksc[2 * st + hh] : ksc[st >> 1]);
-
-    // S^T tile: 4 subtiles of 32 keys.
-    i32x16 sacc[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[st][i] = 0;
-      const int r = 32 * st + col;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const i32x4 kf = *reinterpret_cast<const i32x4*>(ks + r * D + 16 * swz<D>(r, 2 * s + hh));
-        sacc[st] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], sacc[st], 0, 0, 0);
-      }
+      for (int st = 0; st < 4; ++st) cs[st] = dq2 * (thread_gran ? ksc[2 * st + hh] : ksc[st >> 1]);
     }
 
+    // Phase A: dequantise S(t) and take the row maximum, beside the PV product
+    // of tile t-1 (V(t-1) is in slot NXT).  LDS operands are fetched ahead of
+    // use (bias one quad, V fragments one PV interval) so that a quad's vector
+    // work covers their latency.
+    const int vslot_off = R::V0 + NXT * R::V;
     float x[4][16];
+    float mx = -INFINITY;
+    i32x8 vf[2];
+    vf[0] = v_frag(vo, vslot_off, 0, 0);
+    float4 bnext = *reinterpret_cast<const float4*>(lds + aux + bo);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 bv = *reinterpret_cast<const float4*>(bs + 32 * st + 8 * a4 + 4 * hh);
-        x[st][4 * a4 + 0] = static_cast<float>(sacc[st][4 * a4 + 0]) * cs[st] + bv.x;
-        x[st][4 * a4 + 1] = static_cast<float>(sacc[st][4 * a4 + 1]) * cs[st] + bv.y;
-        x[st][4 * a4 + 2] = static_cast<float>(sacc[st][4 * a4 + 2]) * cs[st] + bv.z;
-        x[st][4 * a4 + 3] = static_cast<float>(sacc[st][4 * a4 + 3]) * cs[st] + bv.w;
-        __builtin_amdgcn_sched_barrier(0);   // consume each bias quad before fetching the next
+    for (int i = 0; i < 16; ++i) {
+      const int st = i >> 2, a4 = i & 3;
+      const float4 bv = bnext;
+      if (i + 1 < 16) {
+        const int st1 = (i + 1) >> 2, a1 = (i + 1) & 3;
+        bnext = *reinterpret_cast<const float4*>(lds + aux + bo + 4 * (32 * st1 + 8 * a1));
       }
-    const bool need_mask = (k0 + 128 > a.N) || (a.causal && k0 + 127 > q0 + 32 * w);
+      const int e = i / PV_EVERY;
+      if (i % PV_EVERY == 0 && e + 1 < NPV) vf[(e + 1) & 1] = v_frag(vo, vslot_off, (e + 1) / CT, (e + 1) % CT);
+      float* xs = &x[st][4 * a4];
+      xs[0] = static_cast<float>(S_cur[st][4 * a4 + 0]) * cs[st] + bv.x;
+      xs[1] = static_cast<float>(S_cur[st][4 * a4 + 1]) * cs[st] + bv.y;
+      xs[2] = static_cast<float>(S_cur[st][4 * a4 + 2]) * cs[st] + bv.z;
+      xs[3] = static_cast<float>(S_cur[st][4 * a4 + 3]) * cs[st] + bv.w;
+      mx = fmaxf(mx, fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
+      // The empty asm statements pin each quad's work in place: compiler passes
+      // must not move the matrix or exp2 work across quads or across the
+      // rescale branch, or the interleave is lost.
+      asm volatile("" : "+v"(mx));
+      if (i % PV_EVERY == PV_EVERY - 1) {
+        const int kc = e / CT, c = e % CT;
+        asm volatile("" : "+v"(vf[e & 1]));
+        oacc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[e & 1], pb_prv[kc], oacc[c], 0, 0, 0, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // K fragments of the first two QK MFMAs of phase B.
+    const int kslot_off = R::K0 + NXT * R::K;
+    i32x4 kf[3];
+    kf[0] = k_frag(ko, kslot_off, 0, 0);
+    if (NQK > 1) kf[1] = k_frag(ko, kslot_off, (1 / KS), 1 % KS);
+    // Every wave has read V(t-1) (its slot is refilled in phase B) and this
+    // wave's copies of K(t+1) are complete (only the aux copy issued at the
+    // start of this tile may still run); after the barrier every wave's are.
+    asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    const bool need_mask = (k0 + kTile > a.N) || (a.causal && k0 + kTile - 1 > q0 + 32 * w);
     if (need_mask) {
+      // key j is visible to this query iff j <= lim
+      const int lim = a.causal ? min(a.N - 1, qi) : a.N - 1;
+      mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= a.N || (a.causal && j > qi)) x[st][r] = -INFINITY;
+          x[st][r] = j <= lim ? x[st][r] : -INFINITY;
+          mx = fmaxf(mx, x[st][r]);
         }
     }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[st][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
+    const float mt = fmaxf(mx, __shfl_xor(mx, 32));
+    // The reference maximum moves only when this tile's maximum exceeds it by more than TAU.
+    const float mnew = mt > m + kTau ? mt : m;
     const float alpha = (m == mnew) ? 1.f : ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
-    const float base = (mnew == -INFINITY) ? 0.f : mnew - a.log2_pr;
-    float ps = 0.f;
-    i32x8 pb[2];
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float p0 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 0] - base);
-        const float p1 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 1] - base);
-        const float p2 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 2] - base);
-        const float p3 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 3] - base);
-        ps += (p0 + p1) + (p2 + p3);
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
-        v = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, v, true);
-        pb[st >> 1][4 * (st & 1) + q4] = v;
-      }
-    lsum = alpha * lsum + ps;
-    m = mnew;
-    // Exact skip: when no row maximum of this wave moved, alpha == 1 everywhere.
+    const float base = (mnew == -INFINITY) ? 0.f : mnew + base_shift;
+    // Exact skip: alpha == 1 for every row of this wave unless a reference moved.
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
     }
+    m = mnew;
 
+    // Phase B: exp2 and FP8 packing of tile t, beside the QK product of tile
+    // t+1 (K(t+1) is in slot NXT), subtile by subtile; K fragments are fetched
+    // two MFMAs ahead.
+    float ps = 0.f;
+    const i32x16 zero16 = {};
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const int ch = 32 * c + col;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(vs + ch * 128 + 16 * swz<128>(ch, 4 * kc + 2 * hh));
-        const uint4 v1 = *reinterpret_cast<const uint4*>(vs + ch * 128 + 16 * swz<128>(ch, 4 * kc + 2 * hh + 1));
-        i32x8 va;
-        va[0] = static_cast<int>(v0.x); va[1] = static_cast<int>(v0.y);
-        va[2] = static_cast<int>(v0.z); va[3] = static_cast<int>(v0.w);
-        va[4] = static_cast<int>(v1.x); va[5] = static_cast<int>(v1.y);
-        va[6] = static_cast<int>(v1.z); va[7] = static_cast<int>(v1.w);
-        oacc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[kc], oacc[c], 0, 0, 0, 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      const int st = i >> 2, q4 = i & 3;
+      const int e = i / QK_EVERY;
+      if (i % QK_EVERY == 0 && e + 2 < NQK) kf[(e + 2) % 3] = k_frag(ko, kslot_off, (e + 2) / KS, (e + 2) % KS);
+      // Copies for later tiles, one every 16/(2J) quads: K(t+2) into slot CUR
+      // (K(t) was last read in tile t-1) and V(t+1) into slot NXT (freed at
+      // the mid-tile barrier).
+      if (i % (8 / J) == 0) {
+        const int cj = i / (8 / J);
+        if (cj < J) dma16(src.k, src.k_off, static_cast<uint32_t>(kofs(tt + 2) * D + 4096 * cj),
+                          lds0 + R::K0 + CUR * R::K + (4 * cj + w) * 1024);
+        else dma16(src.v, src.v_off, static_cast<uint32_t>(kofs(tt + 1)) + 32u * (cj - J) * src.v_row,
+                   lds0 + R::V0 + NXT * R::V + (4 * (cj - J) + w) * 1024);
       }
+      const float p0 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 0] - base);
+      const float p1 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 1] - base);
+      const float p2 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 2] - base);
+      const float p3 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 3] - base);
+      ps += (p0 + p1) + (p2 + p3);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, v, true);
+      asm volatile("" : "+v"(v), "+v"(ps));
+      pb_cur[st >> 1][4 * (st & 1) + q4] = v;
+      if (i % QK_EVERY == 0) {
+        const int sn = e / KS, kk = e % KS;
+        asm volatile("" : "+v"(kf[e % 3]));
+        S_nxt[sn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[e % 3], qf[kk], kk == 0 ? zero16 : S_nxt[sn], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    lsum = alpha * lsum + ps;
   };
-  for (int tt = 0; tt < ntiles; tt += 2) {
-    step(tt, buf0, buf1);
-    if (tt + 1 < ntiles) step(tt + 1, buf1, buf0);
+
+  int tt = 0;
+  for (; tt + 1 < ntiles; tt += 2) {
+    tile(tt, std::integral_constant<int, 0>{}, sA, sB, pA, pB);
+    tile(tt + 1, std::integral_constant<int, 1>{}, sB, sA, pB, pA);
+  }
+  if (tt < ntiles) {
+    tile(tt, std::integral_constant<int, 0>{}, sA, sB, pA, pB);
+    pA[0] = pB[0];
+    pA[1] = pB[1];
+  }
+
+  // PV product of the last tile (V(ntiles-1) was copied mid tile ntiles-2).
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  {
+    const int lv = R::V0 + ((ntiles - 1) & 1) * R::V;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        oacc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_frag(vofl, lv, kc, c), pA[kc], oacc[c], 0, 0, 0,
+                                                                  0, 0, 0);
   }
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
