@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // work covers their latency.
     const int vslot_off = R::V0 + NXT * R::V;
     float x[4][16];
-    float mx = -INFINITY;
+    float mx = -INFINITY, mx2 = -INFINITY;
     i32x8 vf[2];
     vf[0] = v_frag(vo, vslot_off, 0, 0);
     float4 bnext = *reinterpret_cast<const float4*>(lds + aux + bo);
@@ -369,14 +369,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       xs[1] = static_cast<float>(S_cur[st][4 * a4 + 1]) * cs[st] + bv.y;
       xs[2] = static_cast<float>(S_cur[st][4 * a4 + 2]) * cs[st] + bv.z;
       xs[3] = static_cast<float>(S_cur[st][4 * a4 + 3]) * cs[st] + bv.w;
-      mx = fmaxf(mx, fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])));
-      // The empty asm statements pin each quad's work in place: compiler passes
-      // must not move the matrix or exp2 work across quads or across the
-      // rescale branch, or the interleave is lost.
-      asm volatile("" : "+v"(mx));
+      mx = fmaxf(fmaxf(mx, xs[0]), xs[1]);
+      mx2 = fmaxf(fmaxf(mx2, xs[2]), xs[3]);
+      // The empty asm statements pin each quad's vector work in place: compiler
+      // passes must not move it across quads or across the rescale branch, or
+      // the interleave with the matrix work is lost.  (Two running maxima keep
+      // the max chains short: two v_max3 per quad.)
+      asm volatile("" : "+v"(mx), "+v"(mx2));
       if (i % PV_EVERY == PV_EVERY - 1) {
         const int kc = e / CT, c = e % CT;
-        asm volatile("" : "+v"(vf[e & 1]));
         oacc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[e & 1], pb_prv[kc], oacc[c], 0, 0, 0, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -391,6 +392,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // start of this tile may still run); after the barrier every wave's are.
     asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
+    mx = fmaxf(mx, mx2);
     const bool need_mask = (k0 + kTile > a.N) || (a.causal && k0 + kTile - 1 > q0 + 32 * w);
     if (need_mask) {
       // key j is visible to this query iff j <= lim
@@ -450,7 +452,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       pb_cur[st >> 1][4 * (st & 1) + q4] = v;
       if (i % QK_EVERY == 0) {
         const int sn = e / KS, kk = e % KS;
-        asm volatile("" : "+v"(kf[e % 3]));
         S_nxt[sn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[e % 3], qf[kk], kk == 0 ? zero16 : S_nxt[sn], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
