@@ -1,0 +1,88 @@
+"""GPU parity at the full benchmark sizes, on sampled heads and query blocks.
+
+Every workload recipe runs at its full size through the same entry points and
+launch configuration bench.py times (default parameters, one workspace).  The
+oracle is independent per head, so for a few sampled heads it recomputes the
+codes, scales and means (compared bit for bit), the bias (within the split
+bf16 bound) and the emulated output of sampled 128-query blocks (within
+2e-3 max|V| plus half an output ulp), plus exact fp64 attention on those rows
+(the GPU must be as accurate as the emulation of the method).  Bars as in
+test_gpu_parity.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.attention import emulate_block, exact_attention_rows
+from oracle.quant import QuantParams
+from quantized_attention_sage_amd.workloads import WORKLOADS, make_inputs
+from gpu_harness import (assert_quant_bit_exact, bias_tolerance_ok, output_tolerance, to_device, log, BUFFERS)
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["llm_prefill", "image_dit", "video_dit", "long_context", "long_context_int4", "target", "target_causal"]
+
+
+def _heads(w):
+    return sorted({(0, 0), (w.B // 2, w.H // 2), (w.B - 1, w.H - 1)})
+
+
+def _blocks(n_blocks):
+    return sorted({0, n_blocks // 2, n_blocks - 1})
+
+
+def _metrics(ref, x):
+    ref = ref.astype(np.float64).ravel()
+    x = x.astype(np.float64).ravel()
+    return float(ref @ x / (np.linalg.norm(ref) * np.linalg.norm(x))), float(np.abs(ref - x).sum() / np.abs(ref).sum())
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_sampled(name):
+    import torch
+    from quantized_attention_sage_amd import api
+
+    w = WORKLOADS[name]
+    log(f"full-size case {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} bits={w.qk_bits}")
+    q, k, v = make_inputs(w)
+    vmax = float(np.abs(v).max())
+    qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
+    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran)
+    shape = api.make_shape(qt, kt, vt)
+    ws = api.Workspace(shape, params, qt.device)
+    out = torch.empty_like(qt)
+    api.quant_qk(qt, kt, vt, params, ws, shape)
+    api.quant_v(vt, params, ws, shape)
+    api.attn_fwd(ws, shape, params, w.causal, out)
+    torch.cuda.synchronize()
+    del qt, kt, vt
+
+    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran)
+    ex_all, gpu_all, em_all = [], [], []
+    for (b, h) in _heads(w):
+        qh, kh, vh = (x[b:b + 1, h:h + 1] for x in (q, k, v))
+        qk1 = oracle.quant_qk(qh, kh, p)
+        vq1 = oracle.quant_v(vh, p)
+        gpu = {n: ws.view(n)[b:b + 1, h:h + 1].cpu().numpy() for n in BUFFERS}
+        assert_quant_bit_exact(gpu, qk1, vq1)
+        ok, worst = bias_tolerance_ok(gpu["bias"], qk1["bias"], qk1["q_mean"], qk1["k_smoothed"])
+        assert ok, f"head {(b, h)}: bias error {worst} of the bound"
+        o_gpu = out[b, h].float().cpu().numpy()
+        for qb in _blocks(qk1["n_pad"] // 128):
+            em, rows = emulate_block(qk1, vq1, 0, 0, qb, w.causal)
+            g = o_gpu[rows]
+            tol = output_tolerance(vh, em, w.dtype) - 2e-3 * float(np.abs(vh).max()) + 2e-3 * vmax
+            bad = np.abs(g - em) > tol
+            assert not bad.any(), (f"head {(b, h)} block {qb}: {int(bad.sum())} outputs beyond tolerance, "
+                                   f"max err {float(np.abs(g - em).max())}")
+            ex = exact_attention_rows(qh[0, 0], kh[0, 0], vh[0, 0], rows, w.causal)
+            ex_all.append(ex)
+            gpu_all.append(g)
+            em_all.append(em)
+        log(f"  head {(b, h)}: codes/scales/means bit-exact, bias within bound, sampled blocks within tolerance")
+    ex_all, gpu_all, em_all = (np.concatenate(x) for x in (ex_all, gpu_all, em_all))
+    cos_g, rl1_g = _metrics(ex_all, gpu_all)
+    cos_e, rl1_e = _metrics(ex_all, em_all)
+    log(f"  vs exact on sampled rows: gpu cos {cos_g:.6f} relL1 {rl1_g:.4f}; emulation cos {cos_e:.6f} relL1 {rl1_e:.4f}")
+    assert cos_g >= min(0.999, cos_e - 2e-4)
+    assert rl1_g <= max(0.02, rl1_e + 0.003)
