@@ -274,19 +274,28 @@ __global__ __launch_bounds__(256) void k_mean_kernel(QKArgs a) {
   if (seg == 0) a.out.k_mean[static_cast<int64_t>(bh) * D + c] = a.smooth_k ? sum / static_cast<float>(a.N) : 0.f;
 }
 
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two-term bf16 split of a pair of floats (hardware conversion, round to
+// nearest even): hi = bf16(x), lo = bf16(x - hi), each returned packed.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2));
 }
 
 // Pass 2, one work-group per (128-key block, head): K' = K - mean, K codes and
 // scales, then the bias dS[qb, j] = mu_Q(qb) . K'_j for the block's keys and
 // every Q block, on the bf16 matrix cores with a three-product hi/lo split of
 // both operands (about 16 significant bits), stored times sm_scale * log2(e).
+// Each wave keeps the split of its 32 keys in registers; the split mu_Q rows
+// go through LDS in chunks of kBiasChunk Q blocks, shared by the four waves.
 // LDS row of D bf16 values (2D bytes): 16-byte chunk c of row r lives at chunk
 // c ^ (r & (2D/16 - 1)), so the 32 rows read together by an MFMA operand load
 // spread over the banks.
+constexpr int kBiasChunk = 64;
+
 template <int D>
 __device__ __forceinline__ int bf_off(int r, int c16) {
   constexpr int CH = 2 * D / 16;
@@ -294,9 +303,11 @@ __device__ __forceinline__ int bf_off(int r, int c16) {
 }
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ahi[32 * 2 * D];   // [32 Q blocks][D] bf16, swizzled rows
-  __shared__ __attribute__((aligned(16))) uint8_t alo[32 * 2 * D];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_quant_bias_kernel(QKArgs a) {
+  constexpr int QC = kBiasChunk;
+  constexpr int PPT = QC * D / 8 / kThreads;    // 8-channel pieces of a mu_Q chunk per thread
+  __shared__ __attribute__((aligned(16))) uint8_t ahi[QC * 2 * D];   // [QC Q blocks][D] bf16, swizzled rows
+  __shared__ __attribute__((aligned(16))) uint8_t alo[QC * 2 * D];
   __shared__ unsigned gmax[128];
   const int blk = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
@@ -304,17 +315,28 @@ __global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
   const int t = threadIdx.x, g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
   const uint16_t* kin = a.k + b * a.ksB + h * a.ksH;
   const float* kmean = a.out.k_mean + static_cast<int64_t>(bh) * D;
+  const float* qmean = a.out.q_mean + static_cast<int64_t>(bh) * a.nblk * D;
   const int valid = min(128, a.N - row0);
   const int w = t / 64, l = t % 64, col = l & 31, hh = l >> 5;
   const int key = 32 * w + col;
-  // Raw K rows in the MFMA operand layout, issued first so their latency
-  // overlaps the quantisation below (the second read of the block hits L2).
-  uint4 kraw[D / 16];
+
+  // The first mu_Q chunk is fetched before the quantisation, so that its
+  // latency overlaps it.
+  float4 mq[PPT][2];
+  auto fetch_mu = [&](int qc0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kraw[ks] = make_uint4(0u, 0u, 0u, 0u);
-    if (key < valid) kraw[ks] = *reinterpret_cast<const uint4*>(kin + static_cast<int64_t>(row0 + key) * a.ksN + 16 * ks + 8 * hh);
-  }
+    for (int i = 0; i < PPT; ++i) {
+      const int piece = t + kThreads * i;
+      const int row = piece / (D / 8), c8 = piece % (D / 8);
+      mq[i][0] = mq[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qc0 + row < a.nblk) {
+        mq[i][0] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qc0 + row) * D + 8 * c8);
+        mq[i][1] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qc0 + row) * D + 8 * c8 + 4);
+      }
+    }
+  };
+  fetch_mu(0);
+
   {
     float x[Tile<D>::TOK][8];
     load_block<D, BF16>(kin, a.ksN, row0, a.N, x);
@@ -332,79 +354,74 @@ __global__ __launch_bounds__(kThreads) void k_quant_bias_kernel(QKArgs a) {
                              a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
   }
 
+  // B operand: the split K' of this wave's 32 keys (the block's rows read
+  // again, from L2), 16 channels per MFMA step, lane half hh holding 8.
   bf16x8 Bhi[D / 16], Blo[D / 16];
   {
     const bool ok = key < valid;
+    uint4 kraw[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kraw[ks] = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) kraw[ks] = *reinterpret_cast<const uint4*>(kin + static_cast<int64_t>(row0 + key) * a.ksN + 16 * ks + 8 * hh);
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int c0 = 16 * ks + 8 * hh;
       const uint16_t* hv = reinterpret_cast<const uint16_t*>(&kraw[ks]);
-      uint16_t bh16[8], bl16[8];
+      const float4 m0 = *reinterpret_cast<const float4*>(kmean + c0);
+      const float4 m1 = *reinterpret_cast<const float4*>(kmean + c0 + 4);
+      const float mk[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      float kp[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kp = ok ? to_f32<BF16>(hv[e]) - kmean[c0 + e] : 0.f;
-        bh16[e] = bf16_rne(kp);
-        bl16[e] = bf16_rne(kp - __uint_as_float(static_cast<uint32_t>(bh16[e]) << 16));
-      }
-      Bhi[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bh16));
-      Blo[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bl16));
+      for (int e = 0; e < 8; ++e) kp[e] = ok ? to_f32<BF16>(hv[e]) - mk[e] : 0.f;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) split_bf16x2(kp[2 * p], kp[2 * p + 1], hi[p], lo[p]);
+      Bhi[ks] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      Blo[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
     }
   }
-  const float* qmean = a.out.q_mean + static_cast<int64_t>(bh) * a.nblk * D;
   float* bias = a.out.bias + static_cast<int64_t>(bh) * a.nblk * a.n_pad + row0 + key;
-  constexpr int APT = 32 * D / 8 / kThreads;    // 8-channel pieces of the mu_Q tile per thread
-  float4 mq[APT][2];
-  auto fetch_mu = [&](int qb0) {
+  for (int qc0 = 0; qc0 < a.nblk; qc0 += QC) {
+    // Split this chunk into LDS (the previous chunk's reads finished at the
+    // barrier ending the last iteration), then fetch the next one.
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
+    for (int i = 0; i < PPT; ++i) {
       const int piece = t + kThreads * i;
       const int row = piece / (D / 8), c8 = piece % (D / 8);
-      mq[i][0] = mq[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (qb0 + row < a.nblk) {
-        mq[i][0] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qb0 + row) * D + 8 * c8);
-        mq[i][1] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qb0 + row) * D + 8 * c8 + 4);
-      }
+      uint32_t hi[4], lo[4];
+      split_bf16x2(mq[i][0].x, mq[i][0].y, hi[0], lo[0]);
+      split_bf16x2(mq[i][0].z, mq[i][0].w, hi[1], lo[1]);
+      split_bf16x2(mq[i][1].x, mq[i][1].y, hi[2], lo[2]);
+      split_bf16x2(mq[i][1].z, mq[i][1].w, hi[3], lo[3]);
+      *reinterpret_cast<uint4*>(ahi + bf_off<D>(row, c8)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(alo + bf_off<D>(row, c8)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
-  };
-  fetch_mu(0);
-  for (int qb0 = 0; qb0 < a.nblk; qb0 += 32) {
-    // The 32 x D mu_Q tile, split into bf16 hi/lo once for all four waves;
-    // the next tile's values are fetched while this one is used.
-#pragma unroll
-    for (int i = 0; i < APT; ++i) {
-      const int piece = t + kThreads * i;
-      const int row = piece / (D / 8), c8 = piece % (D / 8);
-      const float mv[8] = {mq[i][0].x, mq[i][0].y, mq[i][0].z, mq[i][0].w,
-                           mq[i][1].x, mq[i][1].y, mq[i][1].z, mq[i][1].w};
-      uint16_t ah[8], al[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ah[e] = bf16_rne(mv[e]);
-        al[e] = bf16_rne(mv[e] - __uint_as_float(static_cast<uint32_t>(ah[e]) << 16));
-      }
-      *reinterpret_cast<uint4*>(ahi + bf_off<D>(row, c8)) = *reinterpret_cast<const uint4*>(ah);
-      *reinterpret_cast<uint4*>(alo + bf_off<D>(row, c8)) = *reinterpret_cast<const uint4*>(al);
-    }
-    if (qb0 + 32 < a.nblk) fetch_mu(qb0 + 32);
     __syncthreads();
-    f32x16 acc;
+    if (qc0 + QC < a.nblk) fetch_mu(qc0 + QC);
+#pragma unroll 1
+    for (int s0 = 0; s0 < QC && qc0 + s0 < a.nblk; s0 += 32) {
+      f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int c16 = 2 * ks + hh;
-      const bf16x8 A_hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ahi + bf_off<D>(col, c16)));
-      const bf16x8 A_lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(alo + bf_off<D>(col, c16)));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Bhi[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Blo[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_lo, Bhi[ks], acc, 0, 0, 0);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int c16 = 2 * ks + hh;
+        const bf16x8 A_hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ahi + bf_off<D>(s0 + col, c16)));
+        const bf16x8 A_lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(alo + bf_off<D>(s0 + col, c16)));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Bhi[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Blo[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_lo, Bhi[ks], acc, 0, 0, 0);
+      }
+      // acc[i]: Q block qc0 + s0 + 8 (i / 4) + 4 hh + i % 4, this lane's key.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qb = qc0 + s0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (qb < a.nblk) bias[static_cast<int64_t>(qb) * a.n_pad] = acc[i] * a.scale_log2;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qb = qb0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (qb < a.nblk) bias[static_cast<int64_t>(qb) * a.n_pad] = acc[i] * a.scale_log2;
-    }
-    __syncthreads();   // the next tile overwrites ahi/alo
+    __syncthreads();   // every wave is done with this chunk's LDS rows
   }
 }
 
