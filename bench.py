@@ -26,6 +26,23 @@ sys.path.insert(0, ROOT)
 PEAK_TOPS = 5000.0      # MI355X dense INT8 and FP8 matrix peak (both 5.0 P/s)
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30    # calibration copy: reads and writes this many bytes
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+
+
+def quant_bytes(w) -> tuple[int, int]:
+    """Algorithmic HBM bytes of sage_quant_qk and sage_quant_v.
+
+    quant_qk reads Q and K once (2 B/pos each), writes their int8 codes over
+    the padded length (1 B/pos each) and the bias (4 B per query block and
+    key); quant_v reads V once and writes its FP8 codes.  Scales and means
+    (below 0.1 B/pos) are left out, and so are the re-reads of the statistic
+    passes."""
+    n_pad = -(-w.N // 128) * 128
+    bh = w.B * w.H
+    pos, pos_pad = bh * w.N * w.d, bh * n_pad * w.d
+    qk = 4 * pos + 2 * pos_pad + bh * (n_pad // 128) * n_pad * 4
+    v = 2 * pos + pos_pad
+    return qk, v
 COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_counters.json")
 
 
@@ -166,6 +183,7 @@ def main():
     tops = w.ops / (ms_per_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w.name)
+    qk_bytes, v_bytes = quant_bytes(w)
     rec = {
         "metric": "attention TOPS (4*B*H*N^2*d, halved if causal) of quant_qk + quant_v + attn_fwd",
         "value": round(tops, 2),
@@ -186,6 +204,13 @@ def main():
                      "kernel": "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4),
                      "ops_per_launch": w.ops},
         "breakdown_ms": {"quant_qk": round(qk_ms, 4), "quant_v": round(v_ms, 4), "attn_fwd": round(attn_ms, 4)},
+        "quant_roofline": {
+            "bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "quant_qk": {"bytes": qk_bytes, "achieved": round(qk_bytes / (qk_ms * 1e6), 1),
+                         "frac": round(qk_bytes / (qk_ms * 1e6) / PEAK_HBM_GBPS, 4)},
+            "quant_v": {"bytes": v_bytes, "achieved": round(v_bytes / (v_ms * 1e6), 1),
+                        "frac": round(v_bytes / (v_ms * 1e6) / PEAK_HBM_GBPS, 4)},
+        },
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)

@@ -4,6 +4,10 @@
     # kernel durations (rocprofv3 --kernel-trace --stats --output-format csv)
     python profile_counters.py trace <run dir> --workload target --command "<command>" > profiles/<name>.md
 
+    # instruction counters of the attention kernel (one or more --pmc runs)
+    python profile_counters.py sq <run dir> [<run dir> ...] --workload target --command "<command>" ... \
+        > profiles/<name>.md
+
     # HBM traffic of the attention kernel from two counter runs of
     #   bench.py --calibrate-copy  (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)
     python profile_counters.py counters --fetch <run dir> --write <run dir> --workload target \\
@@ -119,6 +123,40 @@ def counters(args):
     print(json.dumps(rec, indent=1))
 
 
+def _tile_waves(w) -> int:
+    """Wave-tiles of the attention kernel: 4 waves per 128-query block, one per 128-key tile it visits."""
+    nblk = -(-w.N // 128)
+    if w.causal:
+        tiles = sum(-(-min(w.N, 128 * (qb + 1)) // 128) for qb in range(nblk))
+    else:
+        tiles = nblk * nblk
+    return w.B * w.H * 4 * tiles
+
+
+def sq(args):
+    from quantized_attention_sage_amd.workloads import WORKLOADS
+    w = WORKLOADS[args.workload]
+    tw = _tile_waves(w)
+    rows = []
+    for run_dir, cmd in zip(args.run_dirs, args.command):
+        names = set()
+        for f in _find(run_dir, "counter_collection.csv"):
+            with open(f) as fh:
+                names |= {r["Counter_Name"] for r in csv.DictReader(fh)}
+        for name in sorted(names):
+            rows.append((name, _pick(_per_dispatch(run_dir, name), ATTN), cmd))
+    print(f"# Instruction counters of attn_fwd_kernel: {args.workload}\n")
+    print(f"Per dispatch (mean over the dispatches of the run); a wave-tile is one wave's share (32 queries) "
+          f"of one 128-key tile, {tw} per dispatch here.\n")
+    print("Commands (repository root, one MI355X):\n")
+    for cmd in args.command:
+        print(f"    {cmd}\n")
+    print("| counter | per dispatch | per wave-tile |")
+    print("|---|---|---|")
+    for name, v, _ in rows:
+        print(f"| {name} | {v:.6g} | {v / tw:.4g} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -126,6 +164,10 @@ def main():
     t.add_argument("run_dir")
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("run_dirs", nargs="+")
+    q.add_argument("--workload", required=True)
+    q.add_argument("--command", required=True, action="append")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -133,7 +175,7 @@ def main():
     c.add_argument("--command-fetch", required=True)
     c.add_argument("--command-write", required=True)
     args = ap.parse_args()
-    trace(args) if args.cmd == "trace" else counters(args)
+    {"trace": trace, "sq": sq, "counters": counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
