@@ -447,18 +447,45 @@ __global__ __launch_bounds__(kThreads) void v_stats_kernel(VArgs a) {
   load_block<D, BF16>(a.v + b * a.sB + h * a.sH, a.sN, row0, a.N, x);
   const int valid = min(128, a.N - row0);
   float mx[8], mn[8];
+  if (valid == 128) {
+    // Whole block: canonicalise each value once, then three-input max/min.
+    float c[Tile<D>::TOK][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mx[e] = -INFINITY;
-    mn[e] = INFINITY;
-  }
+    for (int u = 0; u < Tile<D>::TOK; ++u)
 #pragma unroll
-  for (int u = 0; u < Tile<D>::TOK; ++u) {
-    if (g * Tile<D>::TOK + u < valid) {
+      for (int e = 0; e < 8; ++e) c[u][e] = __builtin_canonicalizef(x[u][e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mx[e] = c[0][e];
+      mn[e] = c[0][e];
+    }
+#pragma unroll
+    for (int u = 1; u + 1 < Tile<D>::TOK; u += 2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        mx[e] = fmaxf(mx[e], x[u][e]);
-        mn[e] = fminf(mn[e], x[u][e]);
+        mx[e] = fmaxf(fmaxf(mx[e], c[u][e]), c[u + 1][e]);
+        mn[e] = fminf(fminf(mn[e], c[u][e]), c[u + 1][e]);
+      }
+    if constexpr (Tile<D>::TOK % 2 == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mx[e] = fmaxf(mx[e], c[Tile<D>::TOK - 1][e]);
+        mn[e] = fminf(mn[e], c[Tile<D>::TOK - 1][e]);
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mx[e] = -INFINITY;
+      mn[e] = INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < Tile<D>::TOK; ++u) {
+      if (g * Tile<D>::TOK + u < valid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mx[e] = fmaxf(mx[e], x[u][e]);
+          mn[e] = fminf(mn[e], x[u][e]);
+        }
       }
     }
   }
