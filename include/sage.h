@@ -43,8 +43,8 @@ extern "C" {
 
 #define SAGE_API __attribute__((visibility("default")))
 
-/* Bumped whenever a buffer layout or a group map below changes. */
-#define SAGE_ABI_VERSION 1
+/* Bumped whenever a buffer layout, a group map or a struct below changes. */
+#define SAGE_ABI_VERSION 2
 
 typedef enum {
   SAGE_OK = 0,
@@ -64,6 +64,17 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1 } sage_dtype;
  *   SAGE_GRAN_WARP:   Q group = 32 consecutive tokens; K group = 64 keys.
  *   SAGE_GRAN_BLOCK:  Q group = 128 consecutive tokens; K group = 64 keys. */
 typedef enum { SAGE_GRAN_THREAD = 0, SAGE_GRAN_WARP = 1, SAGE_GRAN_BLOCK = 2 } sage_gran;
+
+/* Precision of the P~V product.
+ *   SAGE_PV_FP8: SageAttention2 (abstract; SageAttention2++ summary 2.1): V
+ *                smoothed and encoded to FP8 E4M3 per channel, P~ to FP8
+ *                with the fixed scale P_r / 16, FP8 matrix cores.
+ *   SAGE_PV_F16: the SageAttention (first version) setting the SageAttention2
+ *                abstract builds on: P~ and V in the 16-bit type of the shape
+ *                (round to nearest even for P~; V exactly as given, without
+ *                smoothing, so smooth_v and v_range do not apply) on the
+ *                bf16/fp16 matrix cores with fp32 accumulation. */
+typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_F16 = 1 } sage_pv_mode;
 
 /* Shape of Q, K, V ([B, H, N, d], element type dtype).  Strides are in
  * elements for the B, H and N dimensions; the d dimension is contiguous.
@@ -88,6 +99,7 @@ typedef struct {
   float p_range;     /* P_r in (0, 448], default 448: P~ code = E4M3(P~ * P_r / 16) */
   float v_range;     /* V_r in (0, 448], default 448: V code = E4M3(V' V_r/amax) */
   float sm_scale;    /* softmax scale; 0 (default) means 1/sqrt(d)            */
+  int32_t pv_mode;   /* sage_pv_mode, default SAGE_PV_FP8                     */
 } sage_params;
 
 /* Device buffers written by sage_quant_qk (N_pad = 128 * ceil(N / 128)).
@@ -112,13 +124,22 @@ typedef struct {
 } sage_qk_buffers;
 
 /* Device buffers written by sage_quant_v.
+ *   SAGE_PV_FP8:
  *   v_codes  uint8 [B, H, d, N_pad]  E4M3 codes, channel-major.  Within every
  *            64-key group starting at key 64g, byte 32h + t (h in {0,1},
  *            t in 0..31) holds key 64g + 32(t/16) + 8((t%16)/4) + 4h + t%4.
  *            Keys >= N hold 0.
  *   v_scale  fp32  [B, H, d]   amax_c / V_r
  *   v_mean   fp32  [B, H, d]
- *   v_partial fp32 [B, H, N_pad/128, 3, d]   scratch (per-block sum, max, min) */
+ *   v_partial fp32 [B, H, N_pad/128, 3, d]   scratch (per-block sum, max, min)
+ *   SAGE_PV_F16:
+ *   v_codes  16-bit [B, H, d, N_pad]  V itself (the shape's dtype), channel-
+ *            major.  Within every 32-key group starting at key 32g, element
+ *            16m + 8h + 4a + r (m, h, a in {0,1}, r in 0..3) holds key
+ *            32g + 16m + 8a + 4h + r.  Keys >= N hold 0.
+ *   v_scale  fp32  [B, H, d]   1
+ *   v_mean   fp32  [B, H, d]   0
+ *   v_partial                  unused */
 typedef struct {
   uint8_t* v_codes;
   float* v_scale;

@@ -22,6 +22,11 @@ on the codes produced by ``oracle.quant``:
       acc  = alpha * acc + sum_j dec(p^_j) * dec(v^_j)
     O = acc * dV / l + mu_V, rounded once to the output dtype.
 
+With the 16-bit P~V of the first SageAttention (vq["pv"] = "bf16" or "fp16",
+the setting the SageAttention2 abstract starts from) the V codes are V itself,
+P~ = 2^(s - m') is rounded to that type with ties to even instead of being
+scaled and encoded to E4M3, and l sums the fp32 P~ as before.
+
 With tau = 0 this is textbook online softmax (the reference maximum is the
 running maximum).  tau > 0 lets the reference lag the running maximum by up
 to tau (P~ <= 2^tau), which skips most O rescales.  The library's kernel uses
@@ -44,6 +49,18 @@ from .quant import QBLOCK, q_group_index, k_group_index, bias_row
 LOG2E = 1.0 / math.log(2.0)
 DEFAULT_BK = 128
 DEFAULT_TAU = 4.0
+
+
+def round16(x: np.ndarray, kind: str) -> np.ndarray:
+    """Round float32 values to bf16 or fp16 (nearest, ties to even); float64 result."""
+    x = np.ascontiguousarray(x, np.float32)
+    if kind == "fp16":
+        return x.astype(np.float16).astype(np.float64)
+    if kind != "bf16":
+        raise ValueError(kind)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) & np.uint64(0xFFFF0000)
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def _default_scale(d: int, sm_scale):
@@ -105,10 +122,16 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
         dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
         kmat = qk["k_codes"][b, h].astype(np.float64)
         dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
-        vmat = e4m3_decode(vq["v_codes"][b, h])
+        pv16 = vq.get("pv", "fp8") != "fp8"
+        if pv16:
+            vmat = vq["v_values"][b, h].astype(np.float64)
+            pscale = 1.0
+        else:
+            vmat = e4m3_decode(vq["v_codes"][b, h])
+            pscale = float(np.float32(p_range)) * 2.0 ** -tau     # E4M3 code of P~ = E4M3(P~ * pscale)
         dv = vq["v_scale"][b, h].astype(np.float64)
-        pscale = float(np.float32(p_range)) * 2.0 ** -tau     # E4M3 code of P~ = E4M3(P~ * pscale)
     else:
+        pv16 = vq.get("pv", "fp8") != "fp8"
         qmat = qk["q_smoothed"][b, h, q0:q0 + QBLOCK].astype(np.float64)
         dq = np.ones(QBLOCK)
         kmat = qk["k_smoothed"][b, h].astype(np.float64)
@@ -134,7 +157,9 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
         alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - np.where(np.isneginf(m_new), 0.0, m_new)))
         base = np.where(np.isneginf(m_new), 0.0, m_new)
         P = np.exp2(s.astype(np.float64) - base[:, None]).astype(np.float32)
-        if quantized:
+        if pv16:
+            pw = round16(P, vq["pv"])
+        elif quantized:
             pw = e4m3_decode(e4m3_encode((P * np.float32(pscale)).astype(np.float32)))
         else:
             pw = P.astype(np.float64)

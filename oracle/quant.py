@@ -46,6 +46,7 @@ class QuantParams:
     smooth_v: bool = True
     p_range: float = 448.0
     v_range: float = 448.0
+    pv: str = "fp8"          # P~V precision: "fp8" (SageAttention2), or "bf16" / "fp16" (SageAttention)
 
     @property
     def qmax(self) -> int:
@@ -176,11 +177,21 @@ def quant_v(v: np.ndarray, p: QuantParams = QuantParams()):
 
     Returns dict with v_codes (uint8 [B,H,n_pad,d], token-major), v_scale
     ([B,H,d] = amax / V_r), v_mean ([B,H,d]) and v_smoothed (fp32 V').
+
+    With p.pv = "bf16" or "fp16" (the first SageAttention's 16-bit P~V, which
+    the SageAttention2 abstract contrasts with its FP8 one) V is used as given:
+    v_values holds it (fp32, exact, padded rows 0), v_scale is 1 and v_mean 0.
     """
     B, H, N, d = v.shape
     n_pad = n_padded(N)
     valid = np.arange(n_pad) < N
     vp = _pad_tokens(v, n_pad)
+    if p.pv != "fp8":
+        if p.pv not in ("bf16", "fp16"):
+            raise ValueError("pv must be fp8, bf16 or fp16")
+        vals = np.where(valid[:, None], vp, np.float32(0)).astype(np.float32)
+        return dict(v_values=vals, v_scale=np.ones((B, H, d), np.float32), v_mean=np.zeros((B, H, d), np.float32),
+                    v_smoothed=vals, N=N, n_pad=n_pad, pv=p.pv)
     if p.smooth_v:
         v_mean = canonical_mean(vp[..., :N, :], axis=-2, n=N, length=pad_length(N))
     else:
@@ -195,4 +206,4 @@ def quant_v(v: np.ndarray, p: QuantParams = QuantParams()):
     v_codes = e4m3_encode(prod)
     v_codes[..., ~valid, :] = 0
     return dict(v_codes=v_codes, v_scale=v_scale, v_mean=v_mean.astype(np.float32),
-                v_smoothed=vs, N=N, n_pad=n_pad)
+                v_smoothed=vs, N=N, n_pad=n_pad, pv="fp8")

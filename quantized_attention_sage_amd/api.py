@@ -17,11 +17,13 @@ _DTYPES = {torch.float16: L.SAGE_F16, torch.bfloat16: L.SAGE_BF16}
 
 def make_params(qk_bits: int = 8, gran: str = "thread", smooth_q: bool = True, smooth_k: bool = True,
                 smooth_v: bool = True, p_range: float = 448.0, v_range: float = 448.0,
-                sm_scale: float = 0.0) -> L.Params:
+                sm_scale: float = 0.0, pv: str = "fp8") -> L.Params:
     if gran not in L.GRAN:
         raise ValueError(f"granularity must be one of {sorted(L.GRAN)}")
+    if pv not in L.PV_MODE:
+        raise ValueError(f"pv must be one of {sorted(L.PV_MODE)}")
     return L.Params(int(qk_bits), L.GRAN[gran], int(bool(smooth_q)), int(bool(smooth_k)), int(bool(smooth_v)),
-                    float(p_range), float(v_range), float(sm_scale))
+                    float(p_range), float(v_range), float(sm_scale), L.PV_MODE[pv])
 
 
 def _check_tensor(x: torch.Tensor, name: str):
@@ -57,6 +59,7 @@ class Workspace:
         L.check(L.lib().sage_workspace_layout(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(lay)))
         self.layout = lay
         self.shape = (shape.B, shape.H, shape.N, shape.d)
+        self.pv_f16 = params.pv_mode == L.PV_MODE["f16"]
         self.tensor = torch.empty(lay.total_bytes + 256, dtype=torch.uint8, device=device)
         base = self.tensor.data_ptr()
         self._pad = (-base) % 256
@@ -90,7 +93,7 @@ class Workspace:
             "k_mean": (torch.float32, (B, H, d)),
             "bias": (torch.float32, (B, H, nblk, n_pad)),
             "k_partial": (torch.float32, (B, H, nblk, d)),
-            "v_codes": (torch.uint8, (B, H, d, n_pad)),
+            "v_codes": (torch.int16 if self.pv_f16 else torch.uint8, (B, H, d, n_pad)),
             "v_scale": (torch.float32, (B, H, d)),
             "v_mean": (torch.float32, (B, H, d)),
             "v_partial": (torch.float32, (B, H, nblk, 3, d)),

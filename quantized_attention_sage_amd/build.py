@@ -28,6 +28,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-fvisibility=
 SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "attn.hip": [],
+    "attn_pvh.hip": [],
     "sage_api.cpp": ["-x", "hip"],
 }
 

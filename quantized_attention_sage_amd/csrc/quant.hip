@@ -606,6 +606,54 @@ __global__ __launch_bounds__(kThreads) void v_encode_kernel(VArgs a) {
   }
 }
 
+// 16-bit P~V (SAGE_PV_F16): V as given, channel-major, keys of every 32-key
+// group in the order of the 16-bit MFMA operand (swap bits 2 and 3 of the key
+// offset: position 16m + 8h + 4a + r holds key 16m + 8a + 4h + r), zeros past
+// N.  The work-groups of block 0 also write v_scale = 1 and v_mean = 0.
+template <int D>
+__global__ __launch_bounds__(kThreads) void v_pack16_kernel(VArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[D * 128];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int row0 = blk * 128;
+  const int t = threadIdx.x, g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
+  const uint16_t* base = a.v + b * a.sB + h * a.sH;
+  // Four consecutive tokens 4k..4k+3 keep consecutive positions (only bits 2
+  // and 3 swap), so each thread writes them per channel as one 8-byte word.
+#pragma unroll
+  for (int u4 = 0; u4 < Tile<D>::TOK; u4 += 4) {
+    uint4 raw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = row0 + g * Tile<D>::TOK + u4 + j;
+      raw[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < a.N) raw[j] = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * a.sN + 8 * cg);
+    }
+    const int k = g * Tile<D>::TOK + u4;
+    const int pos = (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = reinterpret_cast<const uint16_t*>(&raw[j])[e];
+      *reinterpret_cast<uint2*>(tile + (8 * cg + e) * 128 + pos) = *reinterpret_cast<const uint2*>(v4);
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out.v_codes) + static_cast<int64_t>(bh) * D * a.n_pad + row0;
+#pragma unroll
+  for (int i = 0; i < D * 16 / kThreads; ++i) {
+    const int q = t + kThreads * i;
+    const int c = q >> 4, part = q & 15;
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c) * a.n_pad + 8 * part) =
+        *reinterpret_cast<const uint4*>(tile + c * 128 + 8 * part);
+  }
+  if (blk == 0 && t < D) {
+    a.out.v_scale[static_cast<int64_t>(bh) * D + t] = 1.f;
+    a.out.v_mean[static_cast<int64_t>(bh) * D + t] = 0.f;
+  }
+}
+
 template <int D, bool BF16>
 hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out, hipStream_t st) {
   QKArgs a;
@@ -633,6 +681,10 @@ hipError_t quant_v_impl(const Problem& p, TensorView v, const sage_v_buffers& ou
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.smooth_v = p.smooth_v;
   a.v_range = p.v_range;
   const dim3 grid(p.nblk, p.B * p.H);
+  if (p.pv_f16) {
+    hipLaunchKernelGGL((v_pack16_kernel<D>), grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((v_stats_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((v_finalize_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
   hipLaunchKernelGGL((v_encode_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);

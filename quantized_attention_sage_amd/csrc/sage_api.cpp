@@ -42,6 +42,7 @@ sage_status check_params(const sage_params* p) {
   if (!(p->p_range > 0.f && p->p_range <= 448.f)) return fail(SAGE_EINVAL, "p_range must be in (0, 448]");
   if (!(p->v_range > 0.f && p->v_range <= 448.f)) return fail(SAGE_EINVAL, "v_range must be in (0, 448]");
   if (!(p->sm_scale >= 0.f) || !std::isfinite(p->sm_scale)) return fail(SAGE_EINVAL, "sm_scale must be finite and >= 0");
+  if (p->pv_mode != SAGE_PV_FP8 && p->pv_mode != SAGE_PV_F16) return fail(SAGE_EINVAL, "unknown pv_mode %d", p->pv_mode);
   return SAGE_OK;
 }
 
@@ -76,6 +77,7 @@ sage::Problem make_problem(const sage_shape* s, const sage_params* p) {
   pr.p_range = p->p_range;
   pr.v_range = p->v_range;
   pr.sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  pr.pv_f16 = p->pv_mode == SAGE_PV_F16;
   return pr;
 }
 
@@ -135,6 +137,7 @@ SAGE_API void sage_params_default(sage_params* p) {
   p->p_range = 448.f;
   p->v_range = 448.f;
   p->sm_scale = 0.f;
+  p->pv_mode = SAGE_PV_FP8;
 }
 
 SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_params* p, sage_layout* out) {
@@ -165,7 +168,7 @@ SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_param
   put(L.k_mean, BH * D * 4);
   put(L.bias, BH * nblk * n_pad * 4);
   put(L.k_partial, BH * nblk * D * 4);
-  put(L.v_codes, BH * D * n_pad);
+  put(L.v_codes, BH * D * n_pad * (p->pv_mode == SAGE_PV_F16 ? 2 : 1));
   put(L.v_scale, BH * D * 4);
   put(L.v_mean, BH * D * 4);
   put(L.v_partial, BH * nblk * 3 * D * 4);
@@ -228,7 +231,9 @@ SAGE_API sage_status sage_attn_fwd(const sage_qk_buffers* qk, const sage_v_buffe
     return st;
   if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
   const sage::Problem pr = make_problem(s, p);
-  return launch_result(sage::launch_attn_fwd(pr, *qk, *vb, causal, o, o_stride, static_cast<hipStream_t>(stream)),
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  return launch_result(pr.pv_f16 ? sage::launch_attn_pvh(pr, *qk, *vb, causal, o, o_stride, hs)
+                                 : sage::launch_attn_fwd(pr, *qk, *vb, causal, o, o_stride, hs),
                        "sage_attn_fwd");
 }
 

@@ -40,12 +40,12 @@ def to_device(x: np.ndarray, dtype: str, layout: str = "bhnd"):
 
 
 def run_sage(q, k, v, dtype, causal, qk_bits=8, gran="thread", smooth=(True, True, True), p_range=448.0,
-             v_range=448.0, layout="bhnd", download=BUFFERS):
+             v_range=448.0, layout="bhnd", download=BUFFERS, pv="fp8"):
     import torch
     from quantized_attention_sage_amd import api
     qt, kt, vt = (to_device(x, dtype, layout) for x in (q, k, v))
     params = api.make_params(qk_bits=qk_bits, gran=gran, smooth_q=smooth[0], smooth_k=smooth[1], smooth_v=smooth[2],
-                             p_range=p_range, v_range=v_range)
+                             p_range=p_range, v_range=v_range, pv=pv)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, qt.device)
     api.quant_qk(qt, kt, vt, params, ws, shape)
@@ -71,6 +71,25 @@ def unpermute_v(vc: np.ndarray) -> np.ndarray:
     keys = np.arange(n_pad)
     idx = (keys // 64) * 64 + pos[keys % 64]
     return np.ascontiguousarray(np.swapaxes(vc[..., idx], -1, -2))
+
+
+def unpermute_v16(vc: np.ndarray) -> np.ndarray:
+    """[B,H,d,n_pad] 16-bit V of the 16-bit P~V layout -> [B,H,n_pad,d] uint16, natural order.
+
+    Within each 32-key group, element 16m + 8h + 4a + r holds key 16m + 8a + 4h + r
+    (include/sage.h, SAGE_PV_F16): the key offset with bits 2 and 3 swapped."""
+    n_pad = vc.shape[-1]
+    keys = np.arange(n_pad)
+    idx = (keys & ~12) | ((keys & 4) << 1) | ((keys & 8) >> 1)
+    return np.ascontiguousarray(np.swapaxes(vc.view(np.uint16)[..., idx], -1, -2))
+
+
+def half_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Bit patterns of exactly representable float32 values in fp16 / bf16."""
+    x = np.ascontiguousarray(x, np.float32)
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def bits(x):

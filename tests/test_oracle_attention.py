@@ -222,3 +222,84 @@ def test_planted_softmax_bookkeeping_slips_are_caught(name, monkeypatch):
             if not np.abs(em - ex).max() <= 1e-3:      # NaN counts as caught
                 return
     raise AssertionError(f"planted slip {name!r} went unnoticed")
+
+
+# ------------------------------------------------ 16-bit P~V (first SageAttention)
+# With the 16-bit P~V the only departure from exact attention, once the QK
+# quantiser is switched off, is rounding each P~ to the 16-bit type: every
+# weight moves by at most the unit roundoff u (2^-8 bf16, 2^-11 fp16) relative,
+# while l sums the unrounded P~, so |O - O_exact| <= u max|V| (plus fp32
+# rounding of s and P~).  The bound must hold, and the error must show that
+# the rounding happened at the right precision (well above the next format's u).
+U16 = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
+
+
+def _pv16_error(kind, causal, name="image_dit", N=300):
+    w = scaled(WORKLOADS[name], B=1, H=2, N=N)
+    q, k, v = make_inputs(w)
+    p = QuantParams(pv=kind)
+    qk, vq = oracle.quant_qk(q, k, p), oracle.quant_v(v, p)
+    ex = oracle.exact_attention(q, k, v, causal)
+    em = oracle.emulate_attention(qk, vq, causal, quantized=False)
+    return np.abs(em - ex).max() / np.abs(v).max()
+
+
+def _pv16_floor(causal):
+    # Early causal rows attend to a few keys, so single weights are large and
+    # the rounding error shows at a good fraction of the bound; non-causal rows
+    # average it down further.
+    return 1 / 16 if causal else 1 / 64
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_pv16_emulation_within_rounding_bound(kind, causal):
+    err = _pv16_error(kind, causal)
+    assert err <= U16[kind] * (1 + 1e-3) + 2e-6
+    assert err >= U16[kind] * _pv16_floor(causal)    # the weights really were rounded, at this precision
+
+
+def test_pv16_quant_v_passes_v_through():
+    w = scaled(WORKLOADS["image_dit"], B=1, H=2, N=200)
+    _, _, v = make_inputs(w)
+    vq = oracle.quant_v(v, QuantParams(pv="bf16"))
+    assert vq["v_values"].shape == (1, 2, 256, 128)
+    assert np.array_equal(vq["v_values"][:, :, :200], v.astype(np.float32))
+    assert not vq["v_values"][:, :, 200:].any()
+    assert (vq["v_scale"] == 1).all() and not vq["v_mean"].any()
+
+
+def test_round16_matches_definition():
+    # bf16: keep the top 16 bits of the fp32 word, nearest with ties to even.
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5 - 2 ** -8, 3e-39], np.float32)
+    want = np.array([1.0, 1.0, 1.0 + 2 ** -6, 1.0, -2.5, 0.0], np.float64)
+    got = oracle.attention.round16(x, "bf16")
+    assert np.array_equal(got[:5], want[:5])
+    # a subnormal: word 0x0020AAC8, low half 0xAAC8 above the tie, so the top half rounds up to 0x0021
+    assert np.float32(3e-39).view(np.uint32) == 0x0020AAC8
+    assert got[5] == np.array([0x00210000], np.uint32).view(np.float32)[0]
+    y = np.array([1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 65504.0, 2.0 ** -24], np.float32)
+    assert np.array_equal(oracle.attention.round16(y, "fp16"), [1.0, 1.0 + 2 ** -9, 65504.0, 2.0 ** -24])
+
+
+PV16_MUTATIONS = {
+    "P not rounded": ("pw = round16(P, vq[\"pv\"])", "pw = P.astype(np.float64)"),
+    "rounded to fp16 instead": ("pw = round16(P, vq[\"pv\"])", "pw = round16(P, \"fp16\")"),
+    "weights scaled like FP8 codes": ("pw = round16(P, vq[\"pv\"])", "pw = round16(P * np.float32(28.0), vq[\"pv\"])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PV16_MUTATIONS))
+def test_planted_pv16_slips_are_caught(name, monkeypatch):
+    import inspect
+    import textwrap
+    import oracle.attention as oa
+    old, new = PV16_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(oa.emulate_block))
+    assert src.count(old) == 1, f"mutation anchor for {name!r} not found once"
+    ns = dict(vars(oa))
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    monkeypatch.setattr(oa, "emulate_block", ns["emulate_block"])
+    err = _pv16_error("bf16", True)
+    ok = U16["bf16"] * _pv16_floor(True) <= err <= U16["bf16"] * (1 + 1e-3) + 2e-6
+    assert not ok, f"planted slip {name!r} went unnoticed"
