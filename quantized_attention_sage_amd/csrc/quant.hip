@@ -145,12 +145,20 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
     const int grp = IS_Q ? q_group_in_block(gran, r) : k_group_in_block(gran, r);
     const float am = __uint_as_float(gmax[grp]);
     const float inv = am > 0.f ? qm / am : 0.f;
-    uint32_t packed[2] = {0u, 0u};
+    // code = clamp(rint(x' * inv)) as an exact small integer in fp32, then its
+    // low byte; four bytes per word, assembled with byte permutes.
+    int ci[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float c = rintf(xs[u][e] * inv);
-      c = fminf(fmaxf(c, -qm), qm);
-      packed[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xffu) << (8 * (e & 3));
+    for (int e = 0; e < 8; ++e)
+      ci[e] = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(xs[u][e] * inv), -qm, qm));
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(ci[4 * h + 1]), static_cast<uint32_t>(ci[4 * h]),
+                                                0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(static_cast<uint32_t>(ci[4 * h + 3]),
+                                                static_cast<uint32_t>(ci[4 * h + 2]), 0x04000c0cu);
+      packed[h] = lo | hi;
     }
     *reinterpret_cast<uint2*>(codes_blk + static_cast<int64_t>(r) * D + 8 * cg) = make_uint2(packed[0], packed[1]);
   }
