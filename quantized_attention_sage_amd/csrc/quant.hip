@@ -173,8 +173,9 @@ struct QKArgs {
   float scale_log2;  // sm_scale * log2(e): the bias is stored in the exp2 domain
 };
 
-// Pass 1, one work-group per (128-token block, head): Q block mean, Q codes and
-// scales; per-block K channel sums (subtrees of the K mean's tree).
+// Pass 1, two work-groups per (128-token block, head): blockIdx.z = 0 writes
+// the block's K channel sums (subtrees of the K mean's tree), z = 1 the Q
+// block mean, Q codes and scales.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
   __shared__ float lds[4 * D];
@@ -186,12 +187,15 @@ __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
   float x[Tile<D>::TOK][8];
   float s[8];
 
-  // K block sums.
-  load_block<D, BF16>(a.k + b * a.ksB + h * a.ksH, a.ksN, row0, a.N, x);
-  block_tree_sum<D>(x, s, lds);
-  if (g == 0)
+  if (blockIdx.z == 0) {
+    // K block sums.
+    load_block<D, BF16>(a.k + b * a.ksB + h * a.ksH, a.ksN, row0, a.N, x);
+    block_tree_sum<D>(x, s, lds);
+    if (g == 0)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a.out.k_partial[(static_cast<int64_t>(bh) * a.nblk + blk) * D + 8 * cg + e] = s[e];
+      for (int e = 0; e < 8; ++e) a.out.k_partial[(static_cast<int64_t>(bh) * a.nblk + blk) * D + 8 * cg + e] = s[e];
+    return;
+  }
 
   // Q block mean and codes.
   load_block<D, BF16>(a.q + b * a.qsB + h * a.qsH, a.qsN, row0, a.N, x);
@@ -674,7 +678,7 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.gran = p.gran; a.qmax = p.qmax; a.smooth_q = p.smooth_q; a.smooth_k = p.smooth_k;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
-  hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16>), dim3(p.nblk, p.B * p.H, 2), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
   hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
