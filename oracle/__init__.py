@@ -27,7 +27,7 @@ emulation with the papers' own kernels is "parity unpinned"; what is pinned is
 agreement with exact attention when quantisation is switched off, the
 quantiser invariants, the codec, and the reduction order.
 """
-from . import fp8, reduce, quant, attention, metrics  # noqa: F401
+from . import fp4, fp8, reduce, quant, attention, metrics  # noqa: F401
 
 from .fp8 import e4m3_decode, e4m3_encode  # noqa: F401
 from .reduce import canonical_sum, canonical_mean, pad_length  # noqa: F401

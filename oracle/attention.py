@@ -22,6 +22,11 @@ on the codes produced by ``oracle.quant``:
       acc  = alpha * acc + sum_j dec(p^_j) * dec(v^_j)
     O = acc * dV / l + mu_V, rounded once to the output dtype.
 
+With MXFP4 Q and K (qk["qk_format"] = "mxfp4", the FP4 microscaling of the
+SageAttention3 abstract read as OCP MXFP4, see oracle.fp4) the codes carry
+their own power-of-two block scales: S is the exact dot product of the
+decoded rows and dQ = dK = 1.
+
 With the 16-bit P~V of the first SageAttention (vq["pv"] = "bf16" or "fp16",
 the setting the SageAttention2 abstract starts from) the V codes are V itself,
 P~ = 2^(s - m') is rounded to that type with ties to even instead of being
@@ -112,16 +117,23 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
     smoothing add-backs.
     """
     N, n_pad = qk["N"], qk["n_pad"]
-    d = qk["q_codes"].shape[-1]
+    d = qk["k_mean"].shape[-1]
     scale = _default_scale(d, sm_scale) * LOG2E
     q0 = qb * QBLOCK
     nrows = min(QBLOCK, N - q0)
     qi = q0 + np.arange(QBLOCK)
     if quantized:
-        qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
-        dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
-        kmat = qk["k_codes"][b, h].astype(np.float64)
-        dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
+        if qk.get("qk_format", "int") == "mxfp4":
+            # MXFP4 codes carry their block scales: S is the exact dot product of the decoded rows
+            qmat = qk["q_values"][b, h, q0:q0 + QBLOCK]
+            dq = np.ones(QBLOCK)
+            kmat = qk["k_values"][b, h]
+            dk = np.ones(n_pad)
+        else:
+            qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
+            dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
+            kmat = qk["k_codes"][b, h].astype(np.float64)
+            dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
         pv16 = vq.get("pv", "fp8") != "fp8"
         if pv16:
             vmat = vq["v_values"][b, h].astype(np.float64)
@@ -177,7 +189,8 @@ def emulate_attention(qk: dict, vq: dict, causal: bool, sm_scale=None, p_range: 
 
     Returns float64 [B,H,N,d] (rows of blocks not asked for are NaN).
     """
-    B, H, n_pad, d = qk["q_codes"].shape
+    B, H, n_pad = qk["q_codes"].shape[:3]
+    d = qk["k_mean"].shape[-1]
     N = qk["N"]
     out = np.full((B, H, N, d), np.nan)
     if blocks is None:

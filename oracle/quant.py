@@ -30,6 +30,7 @@ import dataclasses
 
 import numpy as np
 
+from .fp4 import mx_quantize_rows, mx_decode_rows, pack_nibbles
 from .fp8 import e4m3_encode
 from .reduce import canonical_mean, pad_length
 
@@ -47,6 +48,7 @@ class QuantParams:
     p_range: float = 448.0
     v_range: float = 448.0
     pv: str = "fp8"          # P~V precision: "fp8" (SageAttention2), or "bf16" / "fp16" (SageAttention)
+    qk_format: str = "int"   # "int" (INT8 / INT4-range, qk_bits and gran) or "mxfp4" (SageAttention3's FP4)
 
     @property
     def qmax(self) -> int:
@@ -130,7 +132,10 @@ def quant_qk(q: np.ndarray, k: np.ndarray, p: QuantParams = QuantParams(), with_
     B, H, N, d = q.shape
     n_pad = n_padded(N)
     valid = np.arange(n_pad) < N
-    qmax = p.qmax
+    mx = p.qk_format == "mxfp4"
+    if p.qk_format not in ("int", "mxfp4"):
+        raise ValueError("qk_format must be int or mxfp4")
+    qmax = None if mx else p.qmax
     qp = _pad_tokens(q, n_pad)
     kp = _pad_tokens(k, n_pad)
 
@@ -140,7 +145,10 @@ def quant_qk(q: np.ndarray, k: np.ndarray, p: QuantParams = QuantParams(), with_
     else:
         k_mean = np.zeros((B, H, d), np.float32)
     ks = np.where(valid[:, None], (kp - k_mean[..., None, :]).astype(np.float32), np.float32(0))
-    k_codes, k_scale = quantize_rows(ks, valid, k_group_index(n_pad, p.gran), qmax)
+    if mx:
+        k_codes, k_scale = mx_quantize_rows(ks, valid)
+    else:
+        k_codes, k_scale = quantize_rows(ks, valid, k_group_index(n_pad, p.gran), qmax)
 
     # Q: per-channel mean of each 128-token block over its valid tokens.
     nqb = n_pad // QBLOCK
@@ -152,13 +160,21 @@ def quant_qk(q: np.ndarray, k: np.ndarray, p: QuantParams = QuantParams(), with_
         q_mean = np.zeros((B, H, nqb, d), np.float32)
     qs = (qb_view - q_mean[..., None, :]).astype(np.float32).reshape(B, H, n_pad, d)
     qs = np.where(valid[:, None], qs, np.float32(0))
-    q_codes, q_scale = quantize_rows(qs, valid, q_group_index(n_pad, p.gran), qmax)
+    if mx:
+        q_codes, q_scale = mx_quantize_rows(qs, valid)
+    else:
+        q_codes, q_scale = quantize_rows(qs, valid, q_group_index(n_pad, p.gran), qmax)
 
     # Bias that restores the Q mean: dS[qb, j] = sum_c mu_Q[qb, c] * K'[j, c].
     out = dict(q_codes=q_codes, q_scale=q_scale, q_mean=q_mean.astype(np.float32),
                k_codes=k_codes, k_scale=k_scale, k_mean=k_mean.astype(np.float32),
                k_smoothed=ks, q_smoothed=qs, bias=None,
-               N=N, n_pad=n_pad, gran=p.gran, qmax=qmax)
+               N=N, n_pad=n_pad, gran=p.gran, qmax=qmax, qk_format=p.qk_format)
+    if mx:
+        # one 4-bit code per element above; the buffers hold two per byte
+        out["q_values"] = mx_decode_rows(q_codes, q_scale)
+        out["k_values"] = mx_decode_rows(k_codes, k_scale)
+        out["q_codes"], out["k_codes"] = pack_nibbles(q_codes), pack_nibbles(k_codes)
     if with_bias:
         out["bias"] = np.stack([[np.stack([bias_row(out, b, h, qb) for qb in range(nqb)])
                                  for h in range(H)] for b in range(B)])
