@@ -28,23 +28,28 @@ PEAK_BF16_TOPS = 2500.0 # MI355X dense bf16 / fp16 matrix peak
 # With the 16-bit P~V half of the work (QK^T) runs at the INT8 rate and half
 # (P~V) at the bf16 rate: the path's peak is 2 / (1/5000 + 1/2500) TOPS.
 PEAK_PV16_TOPS = 2.0 / (1.0 / PEAK_TOPS + 1.0 / PEAK_BF16_TOPS)
+PEAK_FP4_TOPS = 10100.0 # MI355X dense FP4 matrix peak
+# With MXFP4 Q and K, QK^T runs at the FP4 rate and P~V at the FP8 one.
+PEAK_MXFP4_TOPS = 2.0 / (1.0 / PEAK_FP4_TOPS + 1.0 / PEAK_TOPS)
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30    # calibration copy: reads and writes this many bytes
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
 
-def quant_bytes(w, pv: str = "fp8") -> tuple[int, int]:
+def quant_bytes(w, pv: str = "fp8", qk_format: str = "int") -> tuple[int, int]:
     """Algorithmic HBM bytes of sage_quant_qk and sage_quant_v.
 
     quant_qk reads Q and K once (2 B/pos each), writes their int8 codes over
     the padded length (1 B/pos each) and the bias (4 B per query block and
-    key); quant_v reads V once and writes its FP8 codes (with the 16-bit P~V,
-    V itself in the kernel's layout, 2 B/pos).  Scales and means (below 0.1
+    key; MXFP4 codes are 0.5 B/pos plus a scale byte per 32); quant_v reads V
+    once and writes its FP8 codes (with the 16-bit P~V, V itself in the
+    kernel's layout, 2 B/pos).  Scales and means (below 0.1
     B/pos) are left out, and so are the re-reads of the statistic passes."""
     n_pad = -(-w.N // 128) * 128
     bh = w.B * w.H
     pos, pos_pad = bh * w.N * w.d, bh * n_pad * w.d
-    qk = 4 * pos + 2 * pos_pad + bh * (n_pad // 128) * n_pad * 4
+    codes = 2 * (pos_pad // 2 + pos_pad // 32) if qk_format == "mxfp4" else 2 * pos_pad
+    qk = 4 * pos + codes + bh * (n_pad // 128) * n_pad * 4
     v = 2 * pos + pos_pad * (2 if pv == "f16" else 1)
     return qk, v
 COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_counters.json")
@@ -71,7 +76,7 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, sample_blocks: int = 96, pv: str = "fp8"):
+def cpu_baseline(w, sample_blocks: int = 96, pv: str = "fp8", qk_format: str = "int"):
     """Time the oracle on one head: quantisation of the head plus the tiled
     emulation of `sample_blocks` query blocks, extrapolated to the workload."""
     import numpy as np
@@ -81,7 +86,7 @@ def cpu_baseline(w, sample_blocks: int = 96, pv: str = "fp8"):
 
     one = scaled(w, B=1, H=1)
     q, k, v = make_inputs(one)
-    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran, pv=w.dtype if pv == "f16" else "fp8")
+    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran, pv=w.dtype if pv == "f16" else "fp8", qk_format=qk_format)
     t0 = time.perf_counter()
     qk = oracle.quant_qk(q, k, p, with_bias=False)
     vq = oracle.quant_v(v, p)
@@ -119,6 +124,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qk", choices=("int", "mxfp4"), default="int",
+                    help="Q/K codes: int (INT8 / INT4-range per the workload, the default) or mxfp4 "
+                         "(FP4 E2M1 with an E8M0 scale per 32 channels)")
     ap.add_argument("--pv", choices=("fp8", "f16"), default="fp8",
                     help="P~V precision: fp8 (SageAttention2, the default) or f16 (16-bit P~ and V, "
                          "the first SageAttention's setting)")
@@ -142,7 +150,7 @@ def main():
     q, k, v = make_inputs(w)
     qt, kt, vt = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
     del q, k, v
-    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran, pv=args.pv)
+    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran, pv=args.pv, qk_format=args.qk)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, dev)
     out = torch.empty_like(qt)
@@ -189,10 +197,10 @@ def main():
 
     tops = w.ops / (ms_per_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_ms * 1e-3) / 1e12
-    pv16 = args.pv == "f16"
-    peak = PEAK_PV16_TOPS if pv16 else PEAK_TOPS
-    traffic = None if pv16 else traffic_from_profile(w.name)
-    qk_bytes, v_bytes = quant_bytes(w, args.pv)
+    pv16, mx = args.pv == "f16", args.qk == "mxfp4"
+    peak = PEAK_PV16_TOPS if pv16 else (PEAK_MXFP4_TOPS if mx else PEAK_TOPS)
+    traffic = None if (pv16 or mx) else traffic_from_profile(w.name)
+    qk_bytes, v_bytes = quant_bytes(w, args.pv, args.qk)
     rec = {
         "metric": "attention TOPS (4*B*H*N^2*d, halved if causal) of quant_qk + quant_v + attn_fwd",
         "value": round(tops, 2),
@@ -204,14 +212,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (("int8 QK" if w.qk_bits == 8 else "int4-range QK") +
+        "dtype": (("mxfp4 QK" if mx else ("int8 QK" if w.qk_bits == 8 else "int4-range QK")) +
                   (f" / {w.dtype} PV" if pv16 else " / fp8 PV") + f" ({w.dtype} in/out)"),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "io_dtype": w.dtype, "qk_bits": w.qk_bits, "granularity": w.gran, "pv": args.pv},
+                   "io_dtype": w.dtype, "qk": "mxfp4" if mx else f"int{w.qk_bits}", "granularity": w.gran,
+                   "pv": args.pv},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tops / peak, 4), "traffic": traffic,
-                     "kernel": "attn_pvh_kernel" if pv16 else "attn_fwd_kernel", "kernel_ms": round(attn_ms, 4),
+                     "kernel": "attn_pvh_kernel" if pv16 else ("attn_fp4_kernel" if mx else "attn_fwd_kernel"),
+                     "kernel_ms": round(attn_ms, 4),
                      "ops_per_launch": w.ops},
         "breakdown_ms": {"quant_qk": round(qk_ms, 4), "quant_v": round(v_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "quant_roofline": {
@@ -223,7 +233,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, pv=args.pv)
+        rec["cpu_baseline"] = cpu_baseline(w, pv=args.pv, qk_format=args.qk)
     print(json.dumps(rec), flush=True)
 
 

@@ -44,7 +44,7 @@ extern "C" {
 #define SAGE_API __attribute__((visibility("default")))
 
 /* Bumped whenever a buffer layout, a group map or a struct below changes. */
-#define SAGE_ABI_VERSION 2
+#define SAGE_ABI_VERSION 3
 
 typedef enum {
   SAGE_OK = 0,
@@ -76,6 +76,16 @@ typedef enum { SAGE_GRAN_THREAD = 0, SAGE_GRAN_WARP = 1, SAGE_GRAN_BLOCK = 2 } s
  *                bf16/fp16 matrix cores with fp32 accumulation. */
 typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_F16 = 1 } sage_pv_mode;
 
+/* Format of the Q and K codes.
+ *   SAGE_QK_INT:   integer codes with per-group scales (qk_bits, gran).
+ *   SAGE_QK_MXFP4: the FP4 microscaling of the SageAttention3 abstract, read
+ *                  as OCP MXFP4: E2M1 codes (nearest, ties to even,
+ *                  saturating at 6) and one E8M0 scale 2^(e - 127) per 32
+ *                  channels of a token, with the smallest power of two s such
+ *                  that 6 s >= the block's max |x'|; the QK^T product runs on
+ *                  the scaled FP4 matrix cores.  qk_bits and gran do not apply. */
+typedef enum { SAGE_QK_INT = 0, SAGE_QK_MXFP4 = 1 } sage_qk_format;
+
 /* Shape of Q, K, V ([B, H, N, d], element type dtype).  Strides are in
  * elements for the B, H and N dimensions; the d dimension is contiguous.
  * Every stride must be a multiple of 8 and every tensor pointer 16-byte
@@ -100,6 +110,7 @@ typedef struct {
   float v_range;     /* V_r in (0, 448], default 448: V code = E4M3(V' V_r/amax) */
   float sm_scale;    /* softmax scale; 0 (default) means 1/sqrt(d)            */
   int32_t pv_mode;   /* sage_pv_mode, default SAGE_PV_FP8                     */
+  int32_t qk_format; /* sage_qk_format, default SAGE_QK_INT                   */
 } sage_params;
 
 /* Device buffers written by sage_quant_qk (N_pad = 128 * ceil(N / 128)).
@@ -111,7 +122,13 @@ typedef struct {
  *   k_mean   fp32  [B, H, d]
  *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j] * sm_scale * log2(e)
  *            (the bias in the exp2 domain of the softmax); 0 for j >= N
- *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)   */
+ *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)
+ * With SAGE_QK_MXFP4 the codes and scales of Q and K are instead
+ *   q_codes, k_codes  uint8 [B, H, N_pad, d/2]   E2M1 codes, channel 2i in the
+ *                     low nibble of byte i; rows >= N hold 0
+ *   q_scale, k_scale  uint8 [B, H, N_pad, d/32]  E8M0 scale bytes, one per 32
+ *                     channels of a token; rows >= N hold 0
+ * (the pointers keep their types; the layout reports the byte sizes). */
 typedef struct {
   int8_t* q_codes;
   float* q_scale;

@@ -16,7 +16,8 @@ SAGE_OK, SAGE_EINVAL, SAGE_EUNSUPPORTED, SAGE_EHIP = 0, 1, 2, 3
 SAGE_F16, SAGE_BF16 = 0, 1
 GRAN = {"thread": 0, "warp": 1, "block": 2}
 PV_MODE = {"fp8": 0, "f16": 1}
-ABI_VERSION = 2
+QK_FORMAT = {"int": 0, "mxfp4": 1}
+ABI_VERSION = 3
 
 c_i64_3 = ctypes.c_int64 * 3
 
@@ -30,7 +31,8 @@ class Shape(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("qk_bits", ctypes.c_int32), ("gran", ctypes.c_int32), ("smooth_q", ctypes.c_int32),
                 ("smooth_k", ctypes.c_int32), ("smooth_v", ctypes.c_int32), ("p_range", ctypes.c_float),
-                ("v_range", ctypes.c_float), ("sm_scale", ctypes.c_float), ("pv_mode", ctypes.c_int32)]
+                ("v_range", ctypes.c_float), ("sm_scale", ctypes.c_float), ("pv_mode", ctypes.c_int32),
+                ("qk_format", ctypes.c_int32)]
 
 
 class QKBuffers(ctypes.Structure):

@@ -17,13 +17,15 @@ _DTYPES = {torch.float16: L.SAGE_F16, torch.bfloat16: L.SAGE_BF16}
 
 def make_params(qk_bits: int = 8, gran: str = "thread", smooth_q: bool = True, smooth_k: bool = True,
                 smooth_v: bool = True, p_range: float = 448.0, v_range: float = 448.0,
-                sm_scale: float = 0.0, pv: str = "fp8") -> L.Params:
+                sm_scale: float = 0.0, pv: str = "fp8", qk_format: str = "int") -> L.Params:
     if gran not in L.GRAN:
         raise ValueError(f"granularity must be one of {sorted(L.GRAN)}")
     if pv not in L.PV_MODE:
         raise ValueError(f"pv must be one of {sorted(L.PV_MODE)}")
+    if qk_format not in L.QK_FORMAT:
+        raise ValueError(f"qk_format must be one of {sorted(L.QK_FORMAT)}")
     return L.Params(int(qk_bits), L.GRAN[gran], int(bool(smooth_q)), int(bool(smooth_k)), int(bool(smooth_v)),
-                    float(p_range), float(v_range), float(sm_scale), L.PV_MODE[pv])
+                    float(p_range), float(v_range), float(sm_scale), L.PV_MODE[pv], L.QK_FORMAT[qk_format])
 
 
 def _check_tensor(x: torch.Tensor, name: str):
@@ -60,6 +62,7 @@ class Workspace:
         self.layout = lay
         self.shape = (shape.B, shape.H, shape.N, shape.d)
         self.pv_f16 = params.pv_mode == L.PV_MODE["f16"]
+        self.qk_mx = params.qk_format == L.QK_FORMAT["mxfp4"]
         self.tensor = torch.empty(lay.total_bytes + 256, dtype=torch.uint8, device=device)
         base = self.tensor.data_ptr()
         self._pad = (-base) % 256
@@ -85,10 +88,10 @@ class Workspace:
         sp = getattr(lay, name)
         raw = self.tensor[self._pad + sp.offset: self._pad + sp.offset + sp.bytes]
         shapes = {
-            "q_codes": (torch.int8, (B, H, n_pad, d)),
-            "k_codes": (torch.int8, (B, H, n_pad, d)),
-            "q_scale": (torch.float32, (B, H, lay.q_groups)),
-            "k_scale": (torch.float32, (B, H, lay.k_groups)),
+            "q_codes": (torch.uint8, (B, H, n_pad, d // 2)) if self.qk_mx else (torch.int8, (B, H, n_pad, d)),
+            "k_codes": (torch.uint8, (B, H, n_pad, d // 2)) if self.qk_mx else (torch.int8, (B, H, n_pad, d)),
+            "q_scale": (torch.uint8, (B, H, n_pad, d // 32)) if self.qk_mx else (torch.float32, (B, H, lay.q_groups)),
+            "k_scale": (torch.uint8, (B, H, n_pad, d // 32)) if self.qk_mx else (torch.float32, (B, H, lay.k_groups)),
             "q_mean": (torch.float32, (B, H, nblk, d)),
             "k_mean": (torch.float32, (B, H, d)),
             "bias": (torch.float32, (B, H, nblk, n_pad)),

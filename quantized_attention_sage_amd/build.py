@@ -29,6 +29,7 @@ SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "attn.hip": [],
     "attn_pvh.hip": [],
+    "attn_fp4.hip": [],
     "sage_api.cpp": ["-x", "hip"],
 }
 

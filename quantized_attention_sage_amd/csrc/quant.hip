@@ -164,6 +164,44 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
   }
 }
 
+// MXFP4 quantisation of smoothed rows (SageAttention3 abstract: FP4 with
+// microscaling, read as OCP MXFP4).  Each 32-channel block of a token gets
+// the smallest exponent s with 6 * 2^s >= its max |x| (from the fp32 bit
+// pattern: amax = (1 + M/2^23) 2^e is covered by 1.5 * 2^e iff M <= 2^22),
+// stored as the E8M0 byte s + 127, and the codes E2M1(x * 2^-s) (exact
+// power-of-two scaling, then the hardware conversion: nearest, ties to even,
+// saturating, sign kept).  A thread holds 8 channels of TOK rows; the 4
+// threads of a 32-channel block share the max through lane exchanges.  Row
+// stride of the codes D/2 bytes (channel 2i in the low nibble of byte i), of
+// the scales D/32 bytes.
+template <int D>
+__device__ __forceinline__ void quantize_block_mx(const float (&xs)[Tile<D>::TOK][8], uint8_t* __restrict__ codes_blk,
+                                                  uint8_t* __restrict__ scale_blk) {
+  constexpr int TOK = Tile<D>::TOK, TPR = Tile<D>::TPR;
+  static_assert(TPR % 4 == 0, "a 32-channel block spans 4 threads");
+  const int t = threadIdx.x, g = t / TPR, cg = t % TPR;
+#pragma unroll
+  for (int u = 0; u < TOK; ++u) {
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xs[u][e]));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    const uint32_t bits = __float_as_uint(am);
+    const int ef = static_cast<int>((bits >> 23) & 0xffu);
+    int s = ef - 127 - ((bits & 0x7fffffu) <= 0x400000u ? 2 : 1);
+    s = ef == 0 ? -127 : max(s, -127);
+    uint32_t word = 0u;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(xs[u][0], -s), ldexpf(xs[u][1], -s), 1.f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(xs[u][2], -s), ldexpf(xs[u][3], -s), 1.f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(xs[u][4], -s), ldexpf(xs[u][5], -s), 1.f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(xs[u][6], -s), ldexpf(xs[u][7], -s), 1.f, 3);
+    const int r = g * TOK + u;
+    *reinterpret_cast<uint32_t*>(codes_blk + static_cast<int64_t>(r) * (D / 2) + 4 * cg) = word;
+    if ((cg & 3) == 0) scale_blk[static_cast<int64_t>(r) * (D / 32) + cg / 4] = static_cast<uint8_t>(s + 127);
+  }
+}
+
 struct QKArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -176,7 +214,7 @@ struct QKArgs {
 // Pass 1, two work-groups per (128-token block, head): blockIdx.z = 0 writes
 // the block's K channel sums (subtrees of the K mean's tree), z = 1 the Q
 // block mean, Q codes and scales.
-template <int D, bool BF16>
+template <int D, bool BF16, bool MX>
 __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
   __shared__ float lds[4 * D];
   __shared__ unsigned gmax[128];
@@ -219,9 +257,14 @@ __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[u][e] = ok ? x[u][e] - mu[e] : 0.f;
   }
-  const int ngq = q_groups_per_block(a.gran);
-  quantize_block<D, true>(x, a.gran, a.qmax, gmax, a.out.q_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
-                          a.out.q_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngq);
+  if constexpr (MX) {
+    quantize_block_mx<D>(x, reinterpret_cast<uint8_t*>(a.out.q_codes) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 2),
+                         reinterpret_cast<uint8_t*>(a.out.q_scale) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 32));
+  } else {
+    const int ngq = q_groups_per_block(a.gran);
+    quantize_block<D, true>(x, a.gran, a.qmax, gmax, a.out.q_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+                            a.out.q_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngq);
+  }
 }
 
 // Pairwise tree over the n per-block partial sums of one channel (leaves
@@ -314,7 +357,7 @@ __device__ __forceinline__ int bf_off(int r, int c16) {
   return r * 2 * D + 16 * (c16 ^ (r & (CH - 1)));
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool MX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_quant_bias_kernel(QKArgs a) {
   constexpr int QC = kBiasChunk;
   constexpr int PPT = QC * D / 8 / kThreads;    // 8-channel pieces of a mu_Q chunk per thread
@@ -361,9 +404,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[u][e] = ok ? x[u][e] - mu[e] : 0.f;
     }
-    const int ngk = k_groups_per_block(a.gran);
-    quantize_block<D, false>(x, a.gran, a.qmax, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
-                             a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
+    if constexpr (MX) {
+      quantize_block_mx<D>(x, reinterpret_cast<uint8_t*>(a.out.k_codes) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 2),
+                           reinterpret_cast<uint8_t*>(a.out.k_scale) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 32));
+    } else {
+      const int ngk = k_groups_per_block(a.gran);
+      quantize_block<D, false>(x, a.gran, a.qmax, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+                               a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
+    }
   }
 
   // B operand: the split K' of this wave's 32 keys (the block's rows read
@@ -678,9 +726,15 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.gran = p.gran; a.qmax = p.qmax; a.smooth_q = p.smooth_q; a.smooth_k = p.smooth_k;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
-  hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16>), dim3(p.nblk, p.B * p.H, 2), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16>), grid, dim3(kThreads), 0, st, a);
+  if (p.qk_mx) {
+    hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16, true>), dim3(p.nblk, p.B * p.H, 2), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16, true>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16, false>), dim3(p.nblk, p.B * p.H, 2), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16, false>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -43,6 +43,10 @@ sage_status check_params(const sage_params* p) {
   if (!(p->v_range > 0.f && p->v_range <= 448.f)) return fail(SAGE_EINVAL, "v_range must be in (0, 448]");
   if (!(p->sm_scale >= 0.f) || !std::isfinite(p->sm_scale)) return fail(SAGE_EINVAL, "sm_scale must be finite and >= 0");
   if (p->pv_mode != SAGE_PV_FP8 && p->pv_mode != SAGE_PV_F16) return fail(SAGE_EINVAL, "unknown pv_mode %d", p->pv_mode);
+  if (p->qk_format != SAGE_QK_INT && p->qk_format != SAGE_QK_MXFP4)
+    return fail(SAGE_EINVAL, "unknown qk_format %d", p->qk_format);
+  if (p->qk_format == SAGE_QK_MXFP4 && p->pv_mode != SAGE_PV_FP8)
+    return fail(SAGE_EUNSUPPORTED, "SAGE_QK_MXFP4 is built with SAGE_PV_FP8 only");
   return SAGE_OK;
 }
 
@@ -78,6 +82,7 @@ sage::Problem make_problem(const sage_shape* s, const sage_params* p) {
   pr.v_range = p->v_range;
   pr.sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / std::sqrt(static_cast<float>(s->d));
   pr.pv_f16 = p->pv_mode == SAGE_PV_F16;
+  pr.qk_mx = p->qk_format == SAGE_QK_MXFP4;
   return pr;
 }
 
@@ -138,6 +143,7 @@ SAGE_API void sage_params_default(sage_params* p) {
   p->v_range = 448.f;
   p->sm_scale = 0.f;
   p->pv_mode = SAGE_PV_FP8;
+  p->qk_format = SAGE_QK_INT;
 }
 
 SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_params* p, sage_layout* out) {
@@ -146,8 +152,12 @@ SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_param
   if (!out) return fail(SAGE_EINVAL, "layout output is NULL");
   const int64_t BH = s->B * s->H, D = s->d;
   const int64_t n_pad = (s->N + 127) / 128 * 128, nblk = n_pad / 128;
-  const int64_t gq = p->gran == SAGE_GRAN_THREAD ? n_pad : (p->gran == SAGE_GRAN_WARP ? n_pad / 32 : nblk);
-  const int64_t gk = p->gran == SAGE_GRAN_THREAD ? n_pad / 16 : n_pad / 64;
+  const bool mx = p->qk_format == SAGE_QK_MXFP4;
+  // integer codes: groups of fp32 scales; MXFP4: one scale byte per 32 channels of a token
+  const int64_t gq = mx ? n_pad * D / 32 : (p->gran == SAGE_GRAN_THREAD ? n_pad : (p->gran == SAGE_GRAN_WARP ? n_pad / 32 : nblk));
+  const int64_t gk = mx ? n_pad * D / 32 : (p->gran == SAGE_GRAN_THREAD ? n_pad / 16 : n_pad / 64);
+  const int64_t code_bytes = mx ? n_pad * D / 2 : n_pad * D;
+  const int64_t scale_bytes = mx ? 1 : 4;
   sage_layout L;
   memset(&L, 0, sizeof(L));
   L.n_pad = n_pad;
@@ -160,11 +170,11 @@ SAGE_API sage_status sage_workspace_layout(const sage_shape* s, const sage_param
     sp.bytes = static_cast<size_t>(bytes);
     off = round_up(off + sp.bytes, 256);
   };
-  put(L.q_codes, BH * n_pad * D);
-  put(L.q_scale, BH * gq * 4);
+  put(L.q_codes, BH * code_bytes);
+  put(L.q_scale, BH * gq * scale_bytes);
   put(L.q_mean, BH * nblk * D * 4);
-  put(L.k_codes, BH * n_pad * D);
-  put(L.k_scale, BH * gk * 4);
+  put(L.k_codes, BH * code_bytes);
+  put(L.k_scale, BH * gk * scale_bytes);
   put(L.k_mean, BH * D * 4);
   put(L.bias, BH * nblk * n_pad * 4);
   put(L.k_partial, BH * nblk * D * 4);
@@ -232,8 +242,9 @@ SAGE_API sage_status sage_attn_fwd(const sage_qk_buffers* qk, const sage_v_buffe
   if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
   const sage::Problem pr = make_problem(s, p);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  return launch_result(pr.pv_f16 ? sage::launch_attn_pvh(pr, *qk, *vb, causal, o, o_stride, hs)
-                                 : sage::launch_attn_fwd(pr, *qk, *vb, causal, o, o_stride, hs),
+  return launch_result(pr.qk_mx    ? sage::launch_attn_fp4(pr, *qk, *vb, causal, o, o_stride, hs)
+                       : pr.pv_f16 ? sage::launch_attn_pvh(pr, *qk, *vb, causal, o, o_stride, hs)
+                                   : sage::launch_attn_fwd(pr, *qk, *vb, causal, o, o_stride, hs),
                        "sage_attn_fwd");
 }
 

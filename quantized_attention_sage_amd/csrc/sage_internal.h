@@ -24,12 +24,16 @@ struct Problem {
   int smooth_q, smooth_k, smooth_v;
   float p_range, v_range, sm_scale;
   int pv_f16;                    // 1: P~ and V in the 16-bit input type (SAGE_PV_F16)
+  int qk_mx;                     // 1: MXFP4 Q and K codes (SAGE_QK_MXFP4)
 };
 
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
                            hipStream_t st);
 hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st);
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
+                           void* o, const int64_t o_stride[3], hipStream_t st);
+// The same attention with MXFP4 Q and K codes on the scaled FP4 matrix cores (Problem::qk_mx).
+hipError_t launch_attn_fp4(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
 // The same attention with the 16-bit P~V product (Problem::pv_f16).
 hipError_t launch_attn_pvh(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,

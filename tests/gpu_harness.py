@@ -40,12 +40,12 @@ def to_device(x: np.ndarray, dtype: str, layout: str = "bhnd"):
 
 
 def run_sage(q, k, v, dtype, causal, qk_bits=8, gran="thread", smooth=(True, True, True), p_range=448.0,
-             v_range=448.0, layout="bhnd", download=BUFFERS, pv="fp8"):
+             v_range=448.0, layout="bhnd", download=BUFFERS, pv="fp8", qk_format="int"):
     import torch
     from quantized_attention_sage_amd import api
     qt, kt, vt = (to_device(x, dtype, layout) for x in (q, k, v))
     params = api.make_params(qk_bits=qk_bits, gran=gran, smooth_q=smooth[0], smooth_k=smooth[1], smooth_v=smooth[2],
-                             p_range=p_range, v_range=v_range, pv=pv)
+                             p_range=p_range, v_range=v_range, pv=pv, qk_format=qk_format)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, qt.device)
     api.quant_qk(qt, kt, vt, params, ws, shape)
