@@ -1,8 +1,8 @@
 """MXFP4: FP4 E2M1 elements in 32-element blocks with an E8M0 power-of-two scale.
 
-The SageAttention3 abstract (on the first page) runs attention on FP4 matrix
-cores with microscaling; the pages fix neither the element format nor the
-block size or the scale format.  The plainest reading on gfx950 is the OCP
+The SageAttention3 abstract (on the fugumt page) runs attention on FP4
+matrix cores with microscaling; the pages fix neither the element format nor
+the block size or the scale format.  The plainest reading on gfx950 is the OCP
 microscaling format its scaled matrix instructions take:
 
 * E2M1 element: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, no
