@@ -17,6 +17,8 @@ Two parts, each citing the passage of the pages it follows:
   arithmetic exactly; the attention output is float64 apart from the fp32
   values that decide an FP8 code.
 * ``metrics`` -- cosine similarity, relative L1 and RMSE ("A.2").
+* ``fp4`` -- MXFP4 (E2M1 codes with E8M0 scales per 32 channels) for the FP4
+  microscaling of the SageAttention3 abstract.
 * ``fp8`` -- the OCP E4M3 ("fn") format, decoded from its definition and
   encoded by nearest-value search with ties to the even code.
 

@@ -16,11 +16,14 @@ import oracle
 from oracle.attention import emulate_block, exact_attention_rows
 from oracle.quant import QuantParams
 from quantized_attention_sage_amd.workloads import WORKLOADS, make_inputs
-from gpu_harness import (assert_quant_bit_exact, bias_tolerance_ok, output_tolerance, to_device, log, BUFFERS)
+from gpu_harness import (assert_quant_bit_exact, bias_tolerance_ok, output_tolerance, to_device, log, BUFFERS,
+                         unpermute_v)
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["llm_prefill", "image_dit", "video_dit", "long_context", "long_context_int4", "target", "target_causal"]
+# the other Q/K and P~V formats at the target shape: (recipe, qk_format, pv)
+MODES = [("target", "mxfp4", "fp8"), ("target_causal", "mxfp4", "fp8"), ("target", "int", "f16")]
 
 
 def _heads(w):
@@ -39,15 +42,26 @@ def _metrics(ref, x):
 
 @pytest.mark.parametrize("name", FULL)
 def test_fullsize_sampled(name):
+    _fullsize(name, "int", "fp8")
+
+
+@pytest.mark.parametrize("name,qk_format,pv", MODES)
+def test_fullsize_sampled_formats(name, qk_format, pv):
+    _fullsize(name, qk_format, pv)
+
+
+def _fullsize(name, qk_format, pv):
     import torch
     from quantized_attention_sage_amd import api
+    from gpu_harness import unpermute_v16, half_bits
 
     w = WORKLOADS[name]
-    log(f"full-size case {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} bits={w.qk_bits}")
+    log(f"full-size case {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} bits={w.qk_bits} "
+        f"qk={qk_format} pv={pv}")
     q, k, v = make_inputs(w)
     vmax = float(np.abs(v).max())
     qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
-    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran)
+    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran, qk_format=qk_format, pv=pv)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, qt.device)
     out = torch.empty_like(qt)
@@ -57,14 +71,22 @@ def test_fullsize_sampled(name):
     torch.cuda.synchronize()
     del qt, kt, vt
 
-    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran)
+    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran, qk_format=qk_format, pv=w.dtype if pv == "f16" else "fp8")
     ex_all, gpu_all, em_all = [], [], []
     for (b, h) in _heads(w):
         qh, kh, vh = (x[b:b + 1, h:h + 1] for x in (q, k, v))
         qk1 = oracle.quant_qk(qh, kh, p)
         vq1 = oracle.quant_v(vh, p)
         gpu = {n: ws.view(n)[b:b + 1, h:h + 1].cpu().numpy() for n in BUFFERS}
-        assert_quant_bit_exact(gpu, qk1, vq1)
+        if qk_format == "int" and pv == "fp8":
+            assert_quant_bit_exact(gpu, qk1, vq1)
+        else:
+            for n in ("q_codes", "k_codes", "q_scale", "k_scale", "q_mean", "k_mean"):
+                np.testing.assert_array_equal(gpu[n].view(np.uint8), qk1[n].view(np.uint8), err_msg=n)
+            if pv == "f16":
+                np.testing.assert_array_equal(unpermute_v16(gpu["v_codes"]), half_bits(vq1["v_values"], w.dtype))
+            else:
+                np.testing.assert_array_equal(unpermute_v(gpu["v_codes"]), vq1["v_codes"], err_msg="v codes")
         ok, worst = bias_tolerance_ok(gpu["bias"], qk1["bias"], qk1["q_mean"], qk1["k_smoothed"])
         assert ok, f"head {(b, h)}: bias error {worst} of the bound"
         o_gpu = out[b, h].float().cpu().numpy()
