@@ -144,8 +144,8 @@ def sq(args):
             with open(f) as fh:
                 names |= {r["Counter_Name"] for r in csv.DictReader(fh)}
         for name in sorted(names):
-            rows.append((name, _pick(_per_dispatch(run_dir, name), ATTN), cmd))
-    print(f"# Instruction counters of attn_fwd_kernel: {args.workload}\n")
+            rows.append((name, _pick(_per_dispatch(run_dir, name), args.kernel), cmd))
+    print(f"# Instruction counters of {args.kernel}: {args.workload}\n")
     print(f"Per dispatch (mean over the dispatches of the run); a wave-tile is one wave's share (32 queries) "
           f"of one 128-key tile, {tw} per dispatch here.\n")
     print("Commands (repository root, one MI355X):\n")
@@ -168,6 +168,7 @@ def main():
     q.add_argument("run_dirs", nargs="+")
     q.add_argument("--workload", required=True)
     q.add_argument("--command", required=True, action="append")
+    q.add_argument("--kernel", default=ATTN, help="kernel name to report (default attn_fwd_kernel)")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
