@@ -55,6 +55,7 @@ def test_defaults():
     p = _params()
     assert (p.qk_bits, p.gran, p.smooth_q, p.smooth_k, p.smooth_v) == (8, 0, 1, 1, 1)
     assert (p.p_range, p.v_range, p.sm_scale) == (448.0, 448.0, 0.0)
+    assert (p.pv_mode, p.qk_format) == (0, 0)
 
 
 @pytest.mark.parametrize("gran,gq,gk", [(0, 1024, 64), (1, 32, 16), (2, 8, 16)])
@@ -77,6 +78,24 @@ def test_layout_sizes(gran, gq, gk):
     for (a, b) in zip(spans, spans[1:]):
         assert a[0] + a[1] <= b[0]
     assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "pv16"])
+def test_layout_sizes_other_formats(mode):
+    """MXFP4 codes are 4 bits (d/2 bytes per token) with one scale byte per 32
+    channels; the 16-bit P~V keeps V itself (2 bytes per element)."""
+    B, H, N, d = 2, 3, 1000, 128
+    n_pad, BH = 1024, 6
+    kw = dict(qk_format=1) if mode == "mxfp4" else dict(pv_mode=1)
+    lay = L.Layout()
+    assert L.lib().sage_workspace_layout(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(_params(**kw)),
+                                         ctypes.byref(lay)) == L.SAGE_OK
+    if mode == "mxfp4":
+        assert lay.q_codes.bytes == lay.k_codes.bytes == BH * n_pad * d // 2
+        assert lay.q_scale.bytes == lay.k_scale.bytes == BH * n_pad * d // 32
+        assert lay.v_codes.bytes == BH * d * n_pad
+    else:
+        assert lay.q_codes.bytes == BH * n_pad * d and lay.v_codes.bytes == 2 * BH * d * n_pad
 
 
 def test_bind_workspace_checks():
@@ -110,7 +129,8 @@ def test_bad_shapes_are_rejected(bad):
 
 
 BAD_PARAMS = [dict(qk_bits=6), dict(gran=3), dict(smooth_q=2), dict(p_range=0.0), dict(p_range=449.0),
-              dict(v_range=-1.0), dict(sm_scale=-0.5), dict(sm_scale=float("inf"))]
+              dict(v_range=-1.0), dict(sm_scale=-0.5), dict(sm_scale=float("inf")), dict(pv_mode=2),
+              dict(qk_format=5), dict(qk_format=1, pv_mode=1)]
 
 
 @pytest.mark.parametrize("bad", BAD_PARAMS)
