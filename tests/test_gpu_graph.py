@@ -1,0 +1,65 @@
+"""A whole step captured in a HIP graph.
+
+The entry points allocate nothing and enqueue no memset (only kernels on the
+caller's stream), so serving loops can capture quant_qk + quant_v + attn_fwd
+once and replay them.  Every replay must equal the eager result bit for bit,
+with eager work and synchronisations between replays, and a replay after the
+inputs change in place must equal the eager step on the new inputs.
+"""
+import pytest
+
+from quantized_attention_sage_amd.workloads import WORKLOADS, scaled, make_inputs
+from gpu_harness import to_device, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("qk_format,pv", [("int", "fp8"), ("mxfp4", "fp8"), ("int", "f16")])
+def test_graph_replay_matches_eager(qk_format, pv):
+    import torch
+    from quantized_attention_sage_amd import api
+
+    w = scaled(WORKLOADS["target_causal"], H=2, N=900)
+    log(f"graph case qk={qk_format} pv={pv}: H={w.H} N={w.N} causal={w.causal}")
+    q, k, v = make_inputs(w)
+    qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
+    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran, qk_format=qk_format, pv=pv)
+    shape = api.make_shape(qt, kt, vt)
+    ws = api.Workspace(shape, params, qt.device)
+    out = torch.empty_like(qt)
+
+    def step():
+        api.quant_qk(qt, kt, vt, params, ws, shape)
+        api.quant_v(vt, params, ws, shape)
+        api.attn_fwd(ws, shape, params, w.causal, out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    for r in range(4):
+        out.zero_()
+        ws.tensor.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r} differs from the eager step"
+
+    vt.mul_(2)                       # exact in bf16/fp16: the replay must read the new V
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = out.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(replayed, out)
+    assert not torch.equal(replayed, ref)
