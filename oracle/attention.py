@@ -130,9 +130,14 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
             kmat = qk["k_values"][b, h]
             dk = np.ones(n_pad)
         else:
-            qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
+            if qk.get("qk_format", "int") == "int_e4m3":
+                # integer codes held as E4M3 bytes: decode to the same integers
+                qmat = e4m3_decode(qk["q_codes"][b, h, q0:q0 + QBLOCK])
+                kmat = e4m3_decode(qk["k_codes"][b, h])
+            else:
+                qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
+                kmat = qk["k_codes"][b, h].astype(np.float64)
             dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
-            kmat = qk["k_codes"][b, h].astype(np.float64)
             dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
         pv16 = vq.get("pv", "fp8") != "fp8"
         if pv16:

@@ -227,3 +227,43 @@ def test_planted_quantiser_slips_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, OverflowError):
             caught += 1
     assert caught, f"planted slip {name!r} went unnoticed"
+
+
+# ------------------------------------------------- INT4-range codes held as E4M3
+# E4M3 bytes of the integers 0..7, written out from the format (bias 7, three
+# mantissa bits): 1 = 1.0 x 2^0 -> 0 0111 000; 3 = 1.5 x 2^1 -> 0 1000 100; ...
+E4M3_OF_INT = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48, 5: 0x4A, 6: 0x4C, 7: 0x4E}
+
+
+def test_int_e4m3_byte_table():
+    ints = np.arange(-7, 8)
+    want = np.array([E4M3_OF_INT[abs(i)] | (0x80 if i < 0 else 0) for i in ints], np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_encode(ints.astype(np.float32)), want)
+    np.testing.assert_array_equal(e4m3_decode(want), ints.astype(np.float64))
+
+
+@pytest.mark.parametrize("gran", ["thread", "warp", "block"])
+def test_int_e4m3_holds_the_int4_codes(gran):
+    """The E4M3-held codes are the INT4-range codes byte for byte through the
+    table above, with identical scales, means and bias, and the emulation of
+    the two formats gives identical outputs."""
+    w = scaled(WORKLOADS["image_dit"], B=1, H=2, N=300)
+    q, k, v = make_inputs(w)
+    pi = QuantParams(qk_bits=4, gran=gran)
+    pe = QuantParams(qk_bits=4, gran=gran, qk_format="int_e4m3")
+    a, b = oracle.quant_qk(q, k, pi), oracle.quant_qk(q, k, pe)
+    table = np.array([E4M3_OF_INT[abs(i)] | (0x80 if i < 0 else 0) for i in range(-7, 8)], np.uint8)
+    for n in ("q_codes", "k_codes"):
+        assert b[n].dtype == np.uint8
+        np.testing.assert_array_equal(b[n], table[a[n].astype(np.int64) + 7], err_msg=n)
+    for n in ("q_scale", "k_scale", "q_mean", "k_mean", "bias"):
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+    vq = oracle.quant_v(v, pi)
+    for causal in (False, True):
+        np.testing.assert_array_equal(oracle.emulate_attention(a, vq, causal), oracle.emulate_attention(b, vq, causal))
+
+
+def test_int_e4m3_needs_int4_range():
+    q = np.zeros((1, 1, 128, 64), np.float32)
+    with pytest.raises(ValueError):
+        oracle.quant_qk(q, q, QuantParams(qk_bits=8, qk_format="int_e4m3"))
