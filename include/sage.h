@@ -10,7 +10,8 @@
  *   Q' = Q - mean_block(Q)                        (per channel, per 128-token block qb)
  *   dS[qb, j] = mean_block(Q)(qb) . K'_j          (restores the Q mean)
  *   Q', K'  -> integer codes with per-group scales (INT8, or INT4-range [-7,7]
- *              held in int8 and run on the INT8 matrix cores)
+ *              held in int8 on the INT8 matrix cores or, with SAGE_QK_INT_E4M3,
+ *              held as E4M3 bytes on the FP8 matrix cores, with the same S)
  *   V'  = V - mean_tokens(V); V' -> FP8 E4M3 with per-channel scales
  *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles against a
  *         reference maximum m that moves only when a tile's row maximum exceeds
@@ -44,7 +45,7 @@ extern "C" {
 #define SAGE_API __attribute__((visibility("default")))
 
 /* Bumped whenever a buffer layout, a group map or a struct below changes. */
-#define SAGE_ABI_VERSION 3
+#define SAGE_ABI_VERSION 4
 
 typedef enum {
   SAGE_OK = 0,
@@ -83,8 +84,16 @@ typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_F16 = 1 } sage_pv_mode;
  *                  saturating at 6) and one E8M0 scale 2^(e - 127) per 32
  *                  channels of a token, with the smallest power of two s such
  *                  that 6 s >= the block's max |x'|; the QK^T product runs on
- *                  the scaled FP4 matrix cores.  qk_bits and gran do not apply. */
-typedef enum { SAGE_QK_INT = 0, SAGE_QK_MXFP4 = 1 } sage_qk_format;
+ *                  the scaled FP4 matrix cores.  qk_bits and gran do not apply.
+ *   SAGE_QK_INT_E4M3: the INT4-range integer codes of SAGE_QK_INT (qk_bits
+ *                  must be 4; gran applies), each stored as the E4M3 byte of
+ *                  the same integer (every integer in [-7, 7] is exact in
+ *                  E4M3; code 0 is byte 0x00).  The QK^T product then runs on
+ *                  the FP8 matrix cores with fp32 accumulation; every partial
+ *                  sum is an integer below 2^24, so S is bit-identical to the
+ *                  integer product of SAGE_QK_INT and so is the output.  With
+ *                  SAGE_PV_FP8 only. */
+typedef enum { SAGE_QK_INT = 0, SAGE_QK_MXFP4 = 1, SAGE_QK_INT_E4M3 = 2 } sage_qk_format;
 
 /* Shape of Q, K, V ([B, H, N, d], element type dtype).  Strides are in
  * elements for the B, H and N dimensions; the d dimension is contiguous.
@@ -123,6 +132,7 @@ typedef struct {
  *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j] * sm_scale * log2(e)
  *            (the bias in the exp2 domain of the softmax); 0 for j >= N
  *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)
+ * With SAGE_QK_INT_E4M3 q_codes and k_codes hold E4M3 bytes (same layout).
  * With SAGE_QK_MXFP4 the codes and scales of Q and K are instead
  *   q_codes, k_codes  uint8 [B, H, N_pad, d/2]   E2M1 codes, channel 2i in the
  *                     low nibble of byte i; rows >= N hold 0

@@ -189,11 +189,27 @@ __device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, int k0
   }
 }
 
-template <int D, bool BF16>
+// F8QK: Q and K codes are small integers held as E4M3 bytes, multiplied on
+// v_mfma_f32_32x32x64_f8f6f4 (two 32-channel fragments per instruction).  Every
+// product and partial sum is an integer below 2^24, so the fp32 result equals
+// the integer product exactly and the int->float conversion disappears.
+// The same copy with the K scales spread so that subtile st, lane half h
+// reads entry 2 st + h for every granularity (64-key groups: entry j holds
+// group j / 4).  s_src is wave 2's per-lane source offset.
+__device__ __forceinline__ void copy_aux_spread(uint32_t slot, const TileSrc& s, uint32_t s_src, int k0, int w) {
+  if (w != 2) {
+    dma4(s.b, w == 3 ? (s.b_off & 255u) : s.b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
+  } else {
+    dma4(s.s, s_src, static_cast<uint32_t>(4 * (k0 / kTile)) * s.s_per_tile, slot + 512);
+  }
+}
+
+template <int D, bool BF16, bool F8QK>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;          // 32-channel k-steps of the QK product
+  constexpr int KS = D / 32;          // 32-channel fragments of Q^ and K^ per row
+  constexpr int KSF = F8QK ? KS / 2 : KS;  // QK MFMAs per 32-key subtile
   constexpr int CT = D / 32;          // 32-channel tiles of the output
-  constexpr int NQK = 4 * KS;         // QK MFMAs per tile
+  constexpr int NQK = 4 * KSF;        // QK MFMAs per tile
   constexpr int NPV = 2 * CT;         // PV MFMAs per tile
   constexpr int QK_EVERY = 16 / NQK;  // softmax quads per QK MFMA
   constexpr int PV_EVERY = 16 / NPV;  // dequant quads per PV MFMA
@@ -218,11 +234,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const float* kscale = a.k_scale + static_cast<int64_t>(bh) * n_kscale;
 
   i32x4 qf[KS];
+  i32x8 qf8[KSF];   // F8QK: fragments 2j, 2j+1 as one operand
   {
     const int8_t* qrow = a.q_codes + (static_cast<int64_t>(bh) * a.n_pad + qi) * D;
+    if constexpr (F8QK) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const i32x4*>(qrow + 32 * s + 16 * hh);
+      for (int j = 0; j < KSF; ++j) {
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(qrow + 64 * j + 16 * hh);
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(qrow + 64 * j + 32 + 16 * hh);
+        qf8[j][0] = a0[0]; qf8[j][1] = a0[1]; qf8[j][2] = a0[2]; qf8[j][3] = a0[3];
+        qf8[j][4] = a1[0]; qf8[j][5] = a1[1]; qf8[j][6] = a1[2]; qf8[j][7] = a1[3];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const i32x4*>(qrow + 32 * s + 16 * hh);
+    }
   }
+  auto qf2 = [&](int j) __attribute__((always_inline)) { return qf8[j]; };
   float dq;
   if (a.gran == SAGE_GRAN_THREAD) {
     dq = a.q_scale[static_cast<int64_t>(bh) * a.n_pad + qi];
@@ -247,7 +275,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // tile t-1 (mid-tile).  Tile 0's PV product reads the V slot of tile -1,
   // zero-filled here (its P~ is 0 too).
   copy_k<D>(lds0 + R::K0, src, kofs(0), w);
-  copy_aux(lds0 + R::A0, src, kofs(0), w);
+  // wave 2's K-scale source offsets for copy_aux_spread
+  const uint32_t lane4 = 4u * static_cast<uint32_t>(l);
+  const uint32_t ks_src = lane4 >= 32u ? 0u : (thread_gran ? lane4 : (lane4 >> 4) << 2);
+  if constexpr (F8QK) copy_aux_spread(lds0 + R::A0, src, ks_src, kofs(0), w);
+  else copy_aux(lds0 + R::A0, src, kofs(0), w);
   copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
   copy_v<D>(lds0 + R::V0, src, kofs(0), w);
   {
@@ -278,6 +310,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   auto k_frag = [&](const uint32_t* ko, int slot_off, int st, int kk) __attribute__((always_inline)) {
     return lds_i4(ko[kk] + slot_off + 32 * st * D);
   };
+  // F8QK: channels 64j.. of a key as one 32-byte operand (fragments 2j, 2j+1)
+  auto k_frag2 = [&](const uint32_t* ko, int slot_off, int st, int j) __attribute__((always_inline)) {
+    const i32x4 a0 = lds_i4(ko[2 * j] + slot_off + 32 * st * D);
+    const i32x4 a1 = lds_i4(ko[2 * j + 1] + slot_off + 32 * st * D);
+    i32x8 r;
+    r[0] = a0[0]; r[1] = a0[1]; r[2] = a0[2]; r[3] = a0[3];
+    r[4] = a1[0]; r[5] = a1[1]; r[6] = a1[2]; r[7] = a1[3];
+    return r;
+  };
   auto v_frag = [&](const uint32_t (*vo)[2], int slot_off, int kc, int c) __attribute__((always_inline)) {
     const i32x4 v0 = lds_i4(vo[kc][0] + slot_off + 32 * c * kTile);
     const i32x4 v1 = lds_i4(vo[kc][1] + slot_off + 32 * c * kTile);
@@ -293,7 +334,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-  i32x16 sA[4], sB[4];     // S^T of the tile whose softmax runs next (alternating sets)
+  using SAcc = typename std::conditional<F8QK, f32x16, i32x16>::type;
+  SAcc sA[4], sB[4];       // S^T of the tile whose softmax runs next (alternating sets)
   i32x8 pA[2], pB[2];      // FP8 P~ of the previous tile (alternating sets)
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
@@ -305,14 +347,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   for (int st = 0; st < 4; ++st) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sA[st][i] = 0;
+    if constexpr (F8QK) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-      sA[st] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k_frag(kofl, R::K0, st, kk), qf[kk], sA[st], 0, 0, 0);
+      for (int j = 0; j < KSF; ++j)
+        sA[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_frag2(kofl, R::K0, st, j), qf2(j), sA[st], 0, 0, 0,
+                                                                 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        sA[st] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k_frag(kofl, R::K0, st, kk), qf[kk], sA[st], 0, 0, 0);
+    }
   }
 
   // One tile.  CUR: its ring slot (t % 2); S_cur / S_nxt: S^T of tiles t and
   // t+1; pb_prv / pb_cur: FP8 P~ of tiles t-1 and t.
-  auto tile = [&](const int tt, auto cur_slot, i32x16* S_cur, i32x16* S_nxt, i32x8* pb_prv, i32x8* pb_cur)
+  auto tile = [&](const int tt, auto cur_slot, SAcc* S_cur, SAcc* S_nxt, i32x8* pb_prv, i32x8* pb_cur)
                   __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_slot)::value, NXT = 1 - CUR;
     const int k0 = tt * kTile;
@@ -322,25 +371,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // every wave is done with aux(t-1), whose slot is refilled below.
     if constexpr (J == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    copy_aux(lds0 + R::A0 + NXT * R::AUX, src, kofs(tt + 1), w);
+    if constexpr (F8QK) copy_aux_spread(lds0 + R::A0 + NXT * R::AUX, src, ks_src, kofs(tt + 1), w);
+    else copy_aux(lds0 + R::A0 + NXT * R::AUX, src, kofs(tt + 1), w);
 
     // Fresh copies of the lane offsets: without this the compiler hoists one
     // address register per (slot, fragment) out of the loop and spills them.
+    // (The F8QK form, free of the int->float conversions, fits without them;
+    // with them its own offsets spill instead.)
     uint32_t ko[KS], vo[2][2], bo = 16u * hh;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) { ko[kk] = kofl[kk]; asm volatile("" : "+v"(ko[kk])); }
+    for (int kk = 0; kk < KS; ++kk) { ko[kk] = kofl[kk]; if constexpr (!F8QK) asm volatile("" : "+v"(ko[kk])); }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       vo[kc][0] = vofl[kc][0]; vo[kc][1] = vofl[kc][1];
-      asm volatile("" : "+v"(vo[kc][0]), "+v"(vo[kc][1]));
+      if constexpr (!F8QK) asm volatile("" : "+v"(vo[kc][0]), "+v"(vo[kc][1]));
     }
-    asm volatile("" : "+v"(bo));
+    if constexpr (!F8QK) asm volatile("" : "+v"(bo));
     const int aux = R::A0 + CUR * R::AUX;
     float cs[4];
     {
       const float* ksc = reinterpret_cast<const float*>(lds + aux + 512);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) cs[st] = dq2 * (thread_gran ? ksc[2 * st + hh] : ksc[st >> 1]);
+      for (int st = 0; st < 4; ++st)
+        cs[st] = dq2 * (F8QK ? ksc[2 * st + hh] : (thread_gran ? ksc[2 * st + hh] : ksc[st >> 1]));
     }
 
     // Phase A: dequantise S(t) and take the row maximum, beside the PV product
@@ -385,8 +438,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // K fragments of the first two QK MFMAs of phase B.
     const int kslot_off = R::K0 + NXT * R::K;
     i32x4 kf[3];
-    kf[0] = k_frag(ko, kslot_off, 0, 0);
-    if (NQK > 1) kf[1] = k_frag(ko, kslot_off, (1 / KS), 1 % KS);
+    i32x8 kf2[2];
+    if constexpr (F8QK) {
+      kf2[0] = k_frag2(ko, kslot_off, 0, 0);
+    } else {
+      kf[0] = k_frag(ko, kslot_off, 0, 0);
+      if (NQK > 1) kf[1] = k_frag(ko, kslot_off, (1 / KS), 1 % KS);
+    }
     // Every wave has read V(t-1) (its slot is refilled in phase B) and this
     // wave's copies of K(t+1) are complete (only the aux copy issued at the
     // start of this tile may still run); after the barrier every wave's are.
@@ -425,12 +483,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // t+1 (K(t+1) is in slot NXT), subtile by subtile; K fragments are fetched
     // two MFMAs ahead.
     float ps = 0.f;
-    const i32x16 zero16 = {};
+    const SAcc zero16 = {};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int st = i >> 2, q4 = i & 3;
       const int e = i / QK_EVERY;
-      if (i % QK_EVERY == 0 && e + 2 < NQK) kf[(e + 2) % 3] = k_frag(ko, kslot_off, (e + 2) / KS, (e + 2) % KS);
+      if constexpr (F8QK) {
+        // one MFMA (QK_EVERY quads) ahead
+        if (i % QK_EVERY == 0 && e + 1 < NQK) kf2[(e + 1) & 1] = k_frag2(ko, kslot_off, (e + 1) / KSF, (e + 1) % KSF);
+      } else {
+        if (i % QK_EVERY == 0 && e + 2 < NQK) kf[(e + 2) % 3] = k_frag(ko, kslot_off, (e + 2) / KS, (e + 2) % KS);
+      }
       // Copies for later tiles, one every 16/(2J) quads: K(t+2) into slot CUR
       // (K(t) was last read in tile t-1) and V(t+1) into slot NXT (freed at
       // the mid-tile barrier).
@@ -451,8 +514,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       asm volatile("" : "+v"(v), "+v"(ps));
       pb_cur[st >> 1][4 * (st & 1) + q4] = v;
       if (i % QK_EVERY == 0) {
-        const int sn = e / KS, kk = e % KS;
-        S_nxt[sn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[e % 3], qf[kk], kk == 0 ? zero16 : S_nxt[sn], 0, 0, 0);
+        if constexpr (F8QK) {
+          const int sn = e / KSF, j = e % KSF;
+          S_nxt[sn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf2[e & 1], qf2(j), j == 0 ? zero16 : S_nxt[sn],
+                                                                      0, 0, 0, 0, 0, 0);
+        } else {
+          const int sn = e / KS, kk = e % KS;
+          S_nxt[sn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[e % 3], qf[kk], kk == 0 ? zero16 : S_nxt[sn], 0, 0, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -514,7 +583,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool F8QK>
 hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal, void* o,
                      const int64_t o_stride[3], hipStream_t st) {
   AttnArgs a;
@@ -524,7 +593,7 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.gran = p.gran; a.causal = causal ? 1 : 0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.log2_pr = log2f(p.p_range);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16>), dim3(p.nblk * p.B * p.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, F8QK>), dim3(p.nblk * p.B * p.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -532,10 +601,16 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
 
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st) {
-  if (p.D == 128) return p.bf16 ? attn_impl<128, true>(p, qk, vb, causal, o, o_stride, st)
-                                : attn_impl<128, false>(p, qk, vb, causal, o, o_stride, st);
-  return p.bf16 ? attn_impl<64, true>(p, qk, vb, causal, o, o_stride, st)
-                : attn_impl<64, false>(p, qk, vb, causal, o, o_stride, st);
+  if (p.qk_e4m3) {
+    if (p.D == 128) return p.bf16 ? attn_impl<128, true, true>(p, qk, vb, causal, o, o_stride, st)
+                                  : attn_impl<128, false, true>(p, qk, vb, causal, o, o_stride, st);
+    return p.bf16 ? attn_impl<64, true, true>(p, qk, vb, causal, o, o_stride, st)
+                  : attn_impl<64, false, true>(p, qk, vb, causal, o, o_stride, st);
+  }
+  if (p.D == 128) return p.bf16 ? attn_impl<128, true, false>(p, qk, vb, causal, o, o_stride, st)
+                                : attn_impl<128, false, false>(p, qk, vb, causal, o, o_stride, st);
+  return p.bf16 ? attn_impl<64, true, false>(p, qk, vb, causal, o, o_stride, st)
+                : attn_impl<64, false, false>(p, qk, vb, causal, o, o_stride, st);
 }
 
 }  // namespace sage

@@ -117,7 +117,7 @@ __host__ __device__ __forceinline__ int k_groups_per_block(int gran) { return gr
 // gmax: 128 unsigned in LDS.  Writes the block's codes (N_pad rows, so padded
 // rows get 0) and its group scales.
 template <int D, bool IS_Q>
-__device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8], int gran, int qmax,
+__device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8], int gran, int qmax, bool e4m3,
                                                unsigned* gmax, int8_t* __restrict__ codes_blk,
                                                float* __restrict__ scale_blk) {
   constexpr int TOK = Tile<D>::TOK, TPR = Tile<D>::TPR;
@@ -147,11 +147,25 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
     const float inv = am > 0.f ? qm / am : 0.f;
     // code = clamp(rint(x' * inv)) as an exact small integer in fp32, then its
     // low byte; four bytes per word, assembled with byte permutes.
+    uint32_t packed[2];
+    if (e4m3) {
+      // The same integer codes held as E4M3 bytes (exact for |code| <= 15);
+      // adding +0 turns -0 into +0, so that code 0 is byte 0.
+      float cf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cf[e] = __builtin_amdgcn_fmed3f(rintf(xs[u][e] * inv), -qm, qm) + 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(cf[4 * h], cf[4 * h + 1], 0, false);
+        packed[h] = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cf[4 * h + 2], cf[4 * h + 3], lo, true));
+      }
+      *reinterpret_cast<uint2*>(codes_blk + static_cast<int64_t>(r) * D + 8 * cg) = make_uint2(packed[0], packed[1]);
+      continue;
+    }
     int ci[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       ci[e] = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(xs[u][e] * inv), -qm, qm));
-    uint32_t packed[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(ci[4 * h + 1]), static_cast<uint32_t>(ci[4 * h]),
@@ -208,6 +222,7 @@ struct QKArgs {
   int64_t qsB, qsH, qsN, ksB, ksH, ksN;
   sage_qk_buffers out;
   int H, N, n_pad, nblk, gran, qmax, smooth_q, smooth_k;
+  int e4m3;   // integer codes written as E4M3 bytes (INT4-range only)
   float scale_log2;  // sm_scale * log2(e): the bias is stored in the exp2 domain
 };
 
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
                          reinterpret_cast<uint8_t*>(a.out.q_scale) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 32));
   } else {
     const int ngq = q_groups_per_block(a.gran);
-    quantize_block<D, true>(x, a.gran, a.qmax, gmax, a.out.q_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+    quantize_block<D, true>(x, a.gran, a.qmax, a.e4m3, gmax, a.out.q_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
                             a.out.q_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngq);
   }
 }
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                            reinterpret_cast<uint8_t*>(a.out.k_scale) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 32));
     } else {
       const int ngk = k_groups_per_block(a.gran);
-      quantize_block<D, false>(x, a.gran, a.qmax, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+      quantize_block<D, false>(x, a.gran, a.qmax, a.e4m3, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
                                a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
     }
   }
@@ -724,6 +739,7 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.out = out;
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk;
   a.gran = p.gran; a.qmax = p.qmax; a.smooth_q = p.smooth_q; a.smooth_k = p.smooth_k;
+  a.e4m3 = p.qk_e4m3;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
   if (p.qk_mx) {
