@@ -232,6 +232,42 @@ SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, cons
                                const sage_params* p, int causal, void* o, const int64_t o_stride[3],
                                void* workspace, size_t ws_bytes, void* stream);
 
+/* Result of sage_probe_qk_bits (host memory). */
+typedef struct {
+  double cos_int4, cos_int8;       /* cosine similarity with exact attention, over the probed rows */
+  double rel_l1_int4, rel_l1_int8; /* relative L1 distance sum|O - O'| / sum|O| over the same rows */
+  int32_t qk_bits;                 /* the choice: 4 if cos_int4 >= cos_min, else 8 */
+  int32_t reserved;
+} sage_probe_result;
+
+/* Host only.  Bytes of device scratch sage_probe_qk_bits needs for this shape. */
+SAGE_API sage_status sage_probe_scratch_bytes(const sage_shape* s, size_t* bytes);
+
+/* Adaptive INT4/INT8 choice (SageAttention2 abstract: the QK precision is
+ * picked per layer and timestep from measured accuracy; the metrics are those
+ * of the SageAttention2++ summary, A.2).  On query block q_block (rows
+ * 128 q_block .. 128 q_block + 127 that are < N) of every head it
+ *   1. runs sage_quant_v, then the method with INT8 codes (qk_format
+ *      SAGE_QK_INT) and with INT4-range codes (qk_bits 4, in p->qk_format:
+ *      SAGE_QK_INT or SAGE_QK_INT_E4M3), keeping both outputs in the I/O type;
+ *   2. computes exact attention of the same rows in fp32 (fp32 dot products
+ *      and online softmax, no quantisation, no smoothing);
+ *   3. forms cosine similarity and relative L1 of each output against it over
+ *      all probed rows of all heads (fp64 sums) and chooses INT4-range when
+ *      cos_int4 >= cos_min.
+ * On return *qk and *vb hold the quantisation for the chosen precision: call
+ * sage_attn_fwd with p->qk_bits = result->qk_bits (and qk_format SAGE_QK_INT
+ * when it is 8).  p->qk_bits is ignored; p->pv_mode must be SAGE_PV_FP8.
+ * Blocks the calling thread until the sums are on the host (the stream is
+ * synchronised).  Scratch layout (256-byte aligned spans, in order): the
+ * exact rows fp32 [B, H, 128, d]; the INT4-range and the INT8 outputs,
+ * [B, H, 128, d] of the I/O type; per-split partial rows; per-head and total
+ * fp64 sums.  Rows past N are left unspecified in all of them. */
+SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void* v, const sage_shape* s,
+                                        const sage_params* p, int causal, int64_t q_block, float cos_min,
+                                        const sage_qk_buffers* qk, const sage_v_buffers* vb, void* scratch,
+                                        size_t scratch_bytes, sage_probe_result* result, void* stream);
+
 /* Static description of a status code. */
 SAGE_API const char* sage_status_str(int status);
 

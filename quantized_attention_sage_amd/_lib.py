@@ -57,6 +57,11 @@ class Layout(ctypes.Structure):
                  ("k_groups", ctypes.c_int64)] + [(n, Span) for n in SPANS] + [("total_bytes", ctypes.c_size_t)])
 
 
+class ProbeResult(ctypes.Structure):
+    _fields_ = [("cos_int4", ctypes.c_double), ("cos_int8", ctypes.c_double), ("rel_l1_int4", ctypes.c_double),
+                ("rel_l1_int8", ctypes.c_double), ("qk_bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class SageError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"sage status {status}: {message}")
@@ -81,6 +86,11 @@ EXPORTS = {
     "sage_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
                                  ctypes.POINTER(Params), ctypes.c_int, ctypes.c_void_p,
                                  ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_probe_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]),
+    "sage_probe_qk_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
+                                          ctypes.POINTER(Params), ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                          ctypes.POINTER(QKBuffers), ctypes.POINTER(VBuffers), ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.POINTER(ProbeResult), ctypes.c_void_p]),
     "sage_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "sage_last_error": (ctypes.c_char_p, []),
 }

@@ -147,3 +147,50 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
                               int(bool(causal)), ctypes.c_void_p(out.data_ptr()), _out_strides(out),
                               ctypes.c_void_p(ws.ptr), ctypes.c_size_t(ws.nbytes), ctypes.c_void_p(_stream(q.device))))
     return out
+
+
+class ProbeScratch:
+    """Device scratch of the adaptive INT4/INT8 probe, with views of the probed rows."""
+
+    def __init__(self, shape: L.Shape, device):
+        n = ctypes.c_size_t()
+        L.check(L.lib().sage_probe_scratch_bytes(ctypes.byref(shape), ctypes.byref(n)))
+        self.nbytes = n.value
+        self.tensor = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        self._pad = (-self.tensor.data_ptr()) % 256
+        self.shape = (shape.B, shape.H, shape.d)
+        self.io = torch.bfloat16 if shape.dtype == L.SAGE_BF16 else torch.float16
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr() + self._pad
+
+    def rows(self):
+        """(exact fp32, INT4-range, INT8) rows [B, H, 128, d] as the probe left them."""
+        B, H, d = self.shape
+        n = B * H * 128 * d
+        off, out = 0, []
+        for dt, size in ((torch.float32, 4), (self.io, 2), (self.io, 2)):
+            raw = self.tensor[self._pad + off: self._pad + off + n * size]
+            out.append(raw.view(dt).view(B, H, 128, d))
+            off = (off + n * size + 255) // 256 * 256
+        return tuple(out)
+
+
+def probe_qk_bits(q, k, v, params: L.Params, ws: Workspace, shape: L.Shape, causal: bool, q_block: int,
+                  cos_min: float, scratch: ProbeScratch = None) -> dict:
+    """Adaptive INT4/INT8 choice on query block ``q_block`` of every head.
+
+    Leaves the quantisation of the chosen precision in ``ws``; returns the
+    metrics of both precisions and ``qk_bits``."""
+    scratch = scratch or ProbeScratch(shape, q.device)
+    res = L.ProbeResult()
+    L.check(L.lib().sage_probe_qk_bits(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                       ctypes.c_void_p(v.data_ptr()), ctypes.byref(shape), ctypes.byref(params),
+                                       int(bool(causal)), int(q_block), float(cos_min), ctypes.byref(ws.qk),
+                                       ctypes.byref(ws.vb), ctypes.c_void_p(scratch.ptr),
+                                       ctypes.c_size_t(scratch.nbytes), ctypes.byref(res),
+                                       ctypes.c_void_p(_stream(q.device))))
+    return {"cos_int4": res.cos_int4, "cos_int8": res.cos_int8, "rel_l1_int4": res.rel_l1_int4,
+            "rel_l1_int8": res.rel_l1_int8, "qk_bits": res.qk_bits}
+

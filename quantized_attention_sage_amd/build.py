@@ -30,6 +30,7 @@ SOURCES = {
     "attn.hip": [],
     "attn_pvh.hip": [],
     "attn_fp4.hip": [],
+    "probe.hip": [],
     "sage_api.cpp": ["-x", "hip"],
 }
 

@@ -56,6 +56,7 @@ struct AttnArgs {
   int H, N, n_pad, nblk, gran, causal;
   float scale_log2;  // sm_scale * log2(e)
   float log2_pr;     // log2(P_r)
+  int probe_qb;      // PROBE kernels: the one query block of every head (work-group id = head)
 };
 
 // 16-byte chunk swizzle inside a tile row so that the 16 lanes served together
@@ -204,7 +205,8 @@ __device__ __forceinline__ void copy_aux_spread(uint32_t slot, const TileSrc& s,
   }
 }
 
-template <int D, bool BF16, bool F8QK>
+// PROBE: one work-group per head, on query block a.probe_qb only.
+template <int D, bool BF16, bool F8QK, bool PROBE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // 32-channel fragments of Q^ and K^ per row
   constexpr int KSF = F8QK ? KS / 2 : KS;  // QK MFMAs per 32-key subtile
@@ -221,7 +223,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, held in a scalar register
   int bh, qb;
-  map_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), a.nblk, a.causal, bh, qb);
+  if constexpr (PROBE) {
+    bh = static_cast<int>(blockIdx.x);
+    qb = a.probe_qb;
+  } else {
+    map_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), a.nblk, a.causal, bh, qb);
+  }
   const int q0 = qb * 128;
   const int qi = q0 + 32 * w + col;
 
@@ -585,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool BF16, bool F8QK>
 hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal, void* o,
-                     const int64_t o_stride[3], hipStream_t st) {
+                     const int64_t o_stride[3], hipStream_t st, int probe_qb) {
   AttnArgs a;
   a.q_codes = qk.q_codes; a.q_scale = qk.q_scale; a.k_codes = qk.k_codes; a.k_scale = qk.k_scale;
   a.bias = qk.bias; a.v_codes = vb.v_codes; a.v_scale = vb.v_scale; a.v_mean = vb.v_mean;
@@ -593,24 +600,27 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.gran = p.gran; a.causal = causal ? 1 : 0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.log2_pr = log2f(p.p_range);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, F8QK>), dim3(p.nblk * p.B * p.H), dim3(256), 0, st, a);
+  a.probe_qb = probe_qb;
+  const int grid = probe_qb >= 0 ? p.B * p.H : p.nblk * p.B * p.H;
+  if (probe_qb >= 0) hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, F8QK, true>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, F8QK, false>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
-                           void* o, const int64_t o_stride[3], hipStream_t st) {
+                           void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb) {
   if (p.qk_e4m3) {
-    if (p.D == 128) return p.bf16 ? attn_impl<128, true, true>(p, qk, vb, causal, o, o_stride, st)
-                                  : attn_impl<128, false, true>(p, qk, vb, causal, o, o_stride, st);
-    return p.bf16 ? attn_impl<64, true, true>(p, qk, vb, causal, o, o_stride, st)
-                  : attn_impl<64, false, true>(p, qk, vb, causal, o, o_stride, st);
+    if (p.D == 128) return p.bf16 ? attn_impl<128, true, true>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                                  : attn_impl<128, false, true>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+    return p.bf16 ? attn_impl<64, true, true>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                  : attn_impl<64, false, true>(p, qk, vb, causal, o, o_stride, st, probe_qb);
   }
-  if (p.D == 128) return p.bf16 ? attn_impl<128, true, false>(p, qk, vb, causal, o, o_stride, st)
-                                : attn_impl<128, false, false>(p, qk, vb, causal, o, o_stride, st);
-  return p.bf16 ? attn_impl<64, true, false>(p, qk, vb, causal, o, o_stride, st)
-                : attn_impl<64, false, false>(p, qk, vb, causal, o, o_stride, st);
+  if (p.D == 128) return p.bf16 ? attn_impl<128, true, false>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                                : attn_impl<128, false, false>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+  return p.bf16 ? attn_impl<64, true, false>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                : attn_impl<64, false, false>(p, qk, vb, causal, o, o_stride, st, probe_qb);
 }
 
 }  // namespace sage

@@ -271,6 +271,84 @@ SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, cons
   return sage_attn_fwd(&qk, &vb, s, p, causal, o, o_stride, stream);
 }
 
+SAGE_API sage_status sage_probe_scratch_bytes(const sage_shape* s, size_t* bytes) {
+  sage_status st;
+  if ((st = check_shape(s))) return st;
+  if (!bytes) return fail(SAGE_EINVAL, "bytes is NULL");
+  *bytes = sage::probe_layout(static_cast<int>(s->B), static_cast<int>(s->H), static_cast<int>(s->N),
+                              static_cast<int>(s->d), 2).bytes;
+  return ok();
+}
+
+SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void* v, const sage_shape* s,
+                                        const sage_params* p, int causal, int64_t q_block, float cos_min,
+                                        const sage_qk_buffers* qk, const sage_v_buffers* vb, void* scratch,
+                                        size_t scratch_bytes, sage_probe_result* result, void* stream) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p)) || (st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
+      (st = check_tensor(v, "v")) || (st = check_qk_buffers(qk)) || (st = check_v_buffers(vb)))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  if (p->qk_format != SAGE_QK_INT && p->qk_format != SAGE_QK_INT_E4M3)
+    return fail(SAGE_EUNSUPPORTED, "the probe compares integer codes: qk_format must be SAGE_QK_INT or SAGE_QK_INT_E4M3");
+  if (p->pv_mode != SAGE_PV_FP8) return fail(SAGE_EUNSUPPORTED, "the probe runs with SAGE_PV_FP8");
+  const int64_t nblk = (s->N + 127) / 128;
+  if (q_block < 0 || q_block >= nblk)
+    return fail(SAGE_EINVAL, "q_block must be in [0, %lld) (got %lld)", (long long)nblk, (long long)q_block);
+  if (!std::isfinite(cos_min)) return fail(SAGE_EINVAL, "cos_min must be finite");
+  if (!result) return fail(SAGE_EINVAL, "result is NULL");
+  if (!scratch || !aligned(scratch, 256)) return fail(SAGE_EINVAL, "scratch must be a 256-byte aligned pointer");
+  const sage::ProbeLayout PL = sage::probe_layout(static_cast<int>(s->B), static_cast<int>(s->H),
+                                                  static_cast<int>(s->N), static_cast<int>(s->d), 2);
+  if (scratch_bytes < PL.bytes) return fail(SAGE_EINVAL, "scratch too small: %zu < %zu bytes", scratch_bytes, PL.bytes);
+
+  sage_params p8 = *p, p4 = *p;
+  p8.qk_bits = 8;
+  p8.qk_format = SAGE_QK_INT;
+  p4.qk_bits = 4;
+  const sage::Problem pr8 = make_problem(s, &p8), pr4 = make_problem(s, &p4);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const sage::TensorView qv{q, s->q_stride[0], s->q_stride[1], s->q_stride[2]};
+  const sage::TensorView kv{k, s->k_stride[0], s->k_stride[1], s->k_stride[2]};
+  const sage::TensorView vv{v, s->v_stride[0], s->v_stride[1], s->v_stride[2]};
+  char* base = static_cast<char*>(scratch);
+  // outputs [B, H, 128, d]: the kernel writes row q0 + r at o + (q0 + r) * d, so the
+  // pointer handed over sits q0 rows before the span (only rows >= q0 are written)
+  const int64_t D = s->d, q0 = 128 * q_block;
+  const int64_t os[3] = {s->H * 128 * D, 128 * D, D};
+  const uintptr_t ub = reinterpret_cast<uintptr_t>(base), shift = static_cast<uintptr_t>(q0 * D * 2);
+  void* o4 = reinterpret_cast<void*>(ub + PL.o4 - shift);
+  void* o8 = reinterpret_cast<void*>(ub + PL.o8 - shift);
+  const int qb = static_cast<int>(q_block);
+  hipError_t e;
+  if ((e = sage::launch_quant_v(pr8, vv, *vb, hs)) != hipSuccess) return launch_result(e, "sage_probe_qk_bits (quant_v)");
+  if ((e = sage::launch_quant_qk(pr8, qv, kv, *qk, hs)) != hipSuccess ||
+      (e = sage::launch_attn_fwd(pr8, *qk, *vb, causal, o8, os, hs, qb)) != hipSuccess)
+    return launch_result(e, "sage_probe_qk_bits (INT8 pass)");
+  if ((e = sage::launch_quant_qk(pr4, qv, kv, *qk, hs)) != hipSuccess ||
+      (e = sage::launch_attn_fwd(pr4, *qk, *vb, causal, o4, os, hs, qb)) != hipSuccess)
+    return launch_result(e, "sage_probe_qk_bits (INT4-range pass)");
+  if ((e = sage::launch_probe_reference(pr8, qv, kv, vv, causal, qb, base, hs)) != hipSuccess ||
+      (e = sage::launch_probe_sums(pr8, qb, base, hs)) != hipSuccess)
+    return launch_result(e, "sage_probe_qk_bits (reference)");
+  double sums[8];
+  if ((e = hipMemcpyAsync(sums, base + PL.total, sizeof(sums), hipMemcpyDeviceToHost, hs)) != hipSuccess ||
+      (e = hipStreamSynchronize(hs)) != hipSuccess)
+    return launch_result(e, "sage_probe_qk_bits (sums)");
+  // sums: <o4,r>, |o4|^2, <o8,r>, |o8|^2, |r|^2, |o4-r|_1, |o8-r|_1, |r|_1
+  sage_probe_result r;
+  memset(&r, 0, sizeof(r));
+  r.cos_int4 = sums[0] / std::sqrt(sums[1] * sums[4]);
+  r.cos_int8 = sums[2] / std::sqrt(sums[3] * sums[4]);
+  r.rel_l1_int4 = sums[5] / sums[7];
+  r.rel_l1_int8 = sums[6] / sums[7];
+  r.qk_bits = r.cos_int4 >= static_cast<double>(cos_min) ? 4 : 8;
+  if (r.qk_bits == 8 && (e = sage::launch_quant_qk(pr8, qv, kv, *qk, hs)) != hipSuccess)
+    return launch_result(e, "sage_probe_qk_bits (INT8 codes)");
+  *result = r;
+  return ok();
+}
+
 SAGE_API const char* sage_status_str(int status) {
   switch (status) {
     case SAGE_OK: return "ok";

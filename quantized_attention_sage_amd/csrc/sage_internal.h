@@ -31,13 +31,26 @@ struct Problem {
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
                            hipStream_t st);
 hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st);
+// probe_qb >= 0 runs only query block probe_qb of every head (B*H work-groups).
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
-                           void* o, const int64_t o_stride[3], hipStream_t st);
+                           void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb = -1);
 // The same attention with MXFP4 Q and K codes on the scaled FP4 matrix cores (Problem::qk_mx).
 hipError_t launch_attn_fp4(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
 // The same attention with the 16-bit P~V product (Problem::pv_f16).
 hipError_t launch_attn_pvh(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
+
+// Scratch of the adaptive INT4/INT8 probe (byte offsets, 256-byte aligned).
+struct ProbeLayout {
+  size_t ref, o4, o8, part, sums, total, bytes;
+  int chunk, splits;   // keys per split of the exact reference, number of splits
+};
+ProbeLayout probe_layout(int B, int H, int N, int D, int io_bytes);
+// Exact fp32 attention of query block q_block of every head into scratch + ref.
+hipError_t launch_probe_reference(const Problem& p, TensorView q, TensorView k, TensorView v, int causal, int q_block,
+                                  char* scratch, hipStream_t st);
+// fp64 accuracy sums of the o4 and o8 outputs against ref into scratch + total.
+hipError_t launch_probe_sums(const Problem& p, int q_block, char* scratch, hipStream_t st);
 
 }  // namespace sage

@@ -171,3 +171,53 @@ def test_entry_points_validate_before_launching():
     assert lib.sage_attn(fake, fake, fake, ctypes.byref(sh), ctypes.byref(p), 0, fake, strides, fake, 10,
                          None) == L.SAGE_EINVAL                            # workspace too small
     assert lib.sage_status_str(L.SAGE_EUNSUPPORTED) == b"unsupported"
+
+
+def test_probe_scratch_bytes():
+    """Exact rows fp32, two outputs of the I/O type, per-split partial rows
+    (at most 64 splits of whole 32-key sub-tiles, 1024 keys up to 64K keys)
+    and the fp64 sums, each span 256-byte aligned."""
+    def al(x):
+        return (x + 255) // 256 * 256
+    for (B, H, N, d) in [(2, 3, 1000, 128), (1, 32, 16384, 128), (1, 2, 1 << 20, 64)]:
+        n = ctypes.c_size_t()
+        assert L.lib().sage_probe_scratch_bytes(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(n)) == L.SAGE_OK
+        BH, n_pad = B * H, (N + 127) // 128 * 128
+        chunk = 1024 if n_pad <= 64 * 1024 else ((n_pad + 63) // 64 + 31) // 32 * 32
+        S = -(-n_pad // chunk)
+        assert S <= 64
+        want = al(BH * 128 * d * 4) + 2 * al(BH * 128 * d * 2) + al(S * BH * 128 * (d + 2) * 4) + al(BH * 64) + al(64)
+        assert n.value == want
+
+
+BAD_PROBES = [dict(q_block=-1), dict(q_block=8), dict(qk_format=1), dict(pv_mode=1), dict(cos_min=float("nan")),
+              dict(scratch_bytes=-1), dict(result=False), dict(causal=2)]
+
+
+@pytest.mark.parametrize("bad", BAD_PROBES)
+def test_probe_validates_before_launching(bad):
+    """Every bad argument is refused with no device access (the pointers are
+    never dereferenced)."""
+    lib = L.lib()
+    shape = _shape()       # N = 1000: 8 query blocks
+    lay = L.Layout()
+    kw = {k: v for k, v in bad.items() if k in ("qk_format", "pv_mode")}
+    params = _params(qk_bits=4, **kw)
+    lay_params = _params(qk_bits=4)
+    assert lib.sage_workspace_layout(ctypes.byref(shape), ctypes.byref(lay_params), ctypes.byref(lay)) == L.SAGE_OK
+    qk, vb = L.QKBuffers(), L.VBuffers()
+    base = 1 << 40
+    assert lib.sage_bind_workspace(ctypes.byref(lay), ctypes.c_void_p(base), lay.total_bytes, ctypes.byref(qk),
+                                   ctypes.byref(vb)) == L.SAGE_OK
+    n = ctypes.c_size_t()
+    lib.sage_probe_scratch_bytes(ctypes.byref(shape), ctypes.byref(n))
+    scratch_bytes = n.value + (bad["scratch_bytes"] if "scratch_bytes" in bad else 0)
+    res = L.ProbeResult()
+    st = lib.sage_probe_qk_bits(ctypes.c_void_p(base), ctypes.c_void_p(base), ctypes.c_void_p(base),
+                                ctypes.byref(shape), ctypes.byref(params), bad.get("causal", 0), bad.get("q_block", 0),
+                                bad.get("cos_min", 0.999), ctypes.byref(qk), ctypes.byref(vb),
+                                ctypes.c_void_p(base + (1 << 36)), scratch_bytes,
+                                ctypes.byref(res) if bad.get("result", True) else None, None)
+    assert st in (L.SAGE_EINVAL, L.SAGE_EUNSUPPORTED)
+    assert lib.sage_last_error() != b""
+

@@ -1,0 +1,85 @@
+"""GPU parity of the adaptive INT4/INT8 probe (sage_probe_qk_bits).
+
+The probe runs the method at INT8 and INT4-range on one sampled query block
+of every head, exact fp32 attention of the same rows, and the fp64 accuracy
+sums.  Checked here against the oracle (oracle/adaptive.py) and against the
+library's own full-tensor path:
+  * the exact rows within 1e-5 max|V| of fp64 exact attention;
+  * the INT8 and INT4-range rows bit-identical to the same rows of a normal
+    sage_attn_fwd call at that precision (one kernel, restricted to a block);
+  * cosine similarity within 1e-4 and relative L1 within 1e-3 of the oracle's
+    probe, and the same choice wherever the oracle's cos_int4 is not within
+    1e-4 of cos_min;
+  * on return the workspace holds the codes of the chosen precision.
+"""
+import numpy as np
+import pytest
+
+from oracle import adaptive
+import oracle
+from oracle.quant import QuantParams
+from quantized_attention_sage_amd.workloads import WORKLOADS, scaled, make_inputs
+from gpu_harness import to_device, log
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (recipe, overrides, causal, q_block, cos_min, int4 format)
+    "target_mid_block": ("target", dict(H=2, N=640), False, 2, 0.999, "int"),
+    "image_dit_e4m3": ("image_dit", dict(B=1, H=3, N=600), False, 1, 0.999, "int_e4m3"),
+    "llm_causal_ragged_last": ("llm_prefill", dict(B=2, H=2, N=300), True, 2, 0.99, "int"),
+    "tiny_fp16_d64_first": ("tiny", {}, False, 0, 0.9, "int"),
+    "long_causal_first": ("long_context", dict(H=2, N=1100), True, 0, 0.999, "int_e4m3"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_probe(case):
+    import torch
+    from quantized_attention_sage_amd import api
+    name, kw, causal, qb, cos_min, fmt4 = CASES[case]
+    w = scaled(WORKLOADS[name], **kw)
+    q, k, v = make_inputs(w)
+    log(f"probe case {case}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={causal} block={qb} fmt={fmt4}")
+    qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
+    params = api.make_params(qk_bits=4, gran=w.gran, qk_format=fmt4)
+    shape = api.make_shape(qt, kt, vt)
+    ws = api.Workspace(shape, params, qt.device)
+    scratch = api.ProbeScratch(shape, qt.device)
+    res = api.probe_qk_bits(qt, kt, vt, params, ws, shape, causal, qb, cos_min, scratch)
+    torch.cuda.synchronize()
+    ref, o4, o8 = (x.float().cpu().numpy() for x in scratch.rows())
+    codes_after = ws.view("k_codes").cpu().numpy().view(np.uint8).copy()
+    rows = adaptive.probe_rows(w.N, qb)
+    nr = len(rows)
+
+    # exact rows against fp64
+    ex = adaptive.exact_rows(q, k, v, causal, qb)
+    err = np.abs(ref[:, :, :nr] - ex).max()
+    log(f"  exact rows: max err {err:.2e} (1e-5 max|V| = {1e-5 * np.abs(v).max():.2e})")
+    assert err <= 1e-5 * np.abs(v).max()
+
+    # the quantized rows equal those of the normal full-tensor call
+    for bits, fmt, got in ((4, fmt4, o4), (8, "int", o8)):
+        p = api.make_params(qk_bits=bits, gran=w.gran, qk_format=fmt)
+        ws2 = api.Workspace(shape, p, qt.device)
+        out = torch.empty_like(qt)
+        api.quant_qk(qt, kt, vt, p, ws2, shape)
+        api.quant_v(vt, p, ws2, shape)
+        api.attn_fwd(ws2, shape, p, causal, out)
+        torch.cuda.synchronize()
+        full = out.float().cpu().numpy()[:, :, rows]
+        np.testing.assert_array_equal(got[:, :, :nr], full, err_msg=f"INT{bits} rows differ from the full call")
+        if bits == res["qk_bits"]:
+            np.testing.assert_array_equal(codes_after, ws2.view("k_codes").cpu().numpy().view(np.uint8),
+                                          err_msg="workspace does not hold the chosen codes")
+
+    # metrics and choice against the oracle
+    want = adaptive.probe_qk_bits(q, k, v, w.dtype, causal, qb, cos_min, gran=w.gran, qk4_format=fmt4)
+    log(f"  gpu {res}\n  oracle {want}")
+    for key in ("cos_int4", "cos_int8"):
+        assert abs(res[key] - want[key]) <= 1e-4, key
+    for key in ("rel_l1_int4", "rel_l1_int8"):
+        assert abs(res[key] - want[key]) <= 1e-3, key
+    if abs(want["cos_int4"] - cos_min) > 1e-4:
+        assert res["qk_bits"] == want["qk_bits"]
