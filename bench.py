@@ -117,6 +117,33 @@ def cpu_baseline(w, sample_blocks: int = 96, pv: str = "fp8", qk_format: str = "
             "seconds_measured": round(t_quant + t_blocks, 2), "seconds_extrapolated": round(t_total, 1)}
 
 
+def probe_bench(args, w, qt, kt, vt, shape, ws, dev):
+    """Time sage_probe_qk_bits (it synchronises the stream itself) on the middle
+    query block.  The exact reference is the probe's fp32 vector-ALU part:
+    4 * B * H * rows * keys * d flops (QK dot products and the P V sums)."""
+    import torch
+    from quantized_attention_sage_amd import api
+    params = api.make_params(qk_bits=4, gran=w.gran, qk_format="int_e4m3" if w.qk_bits == 4 else "int")
+    scratch = api.ProbeScratch(shape, dev)
+    qb = (w.N - 1) // 128 // 2
+    for _ in range(args.warmup):
+        api.probe_qk_bits(qt, kt, vt, params, ws, shape, w.causal, qb, args.cos_min, scratch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = api.probe_qk_bits(qt, kt, vt, params, ws, shape, w.causal, qb, args.cos_min, scratch)
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    rows = min(128, w.N - 128 * qb)
+    keys = min(w.N, 128 * qb + 128) if w.causal else w.N
+    ref_flops = 4 * w.B * w.H * rows * keys * w.d
+    print(json.dumps({"metric": "adaptive INT4/INT8 probe time (sage_probe_qk_bits, host-synchronised)",
+                      "value": round(ms, 4), "unit": "ms", "higher_is_better": False, "steps": args.steps,
+                      "warmup": args.warmup, "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N,
+                                                         "d": w.d, "causal": w.causal, "q_block": qb,
+                                                         "cos_min": args.cos_min},
+                      "reference_flops": ref_flops, "result": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +158,10 @@ def main():
     ap.add_argument("--pv", choices=("fp8", "f16"), default="fp8",
                     help="P~V precision: fp8 (SageAttention2, the default) or f16 (16-bit P~ and V, "
                          "the first SageAttention's setting)")
+    ap.add_argument("--probe", action="store_true",
+                    help="time the adaptive INT4/INT8 probe (sage_probe_qk_bits on the middle query block) "
+                         "instead of the step, and print its own JSON line")
+    ap.add_argument("--cos-min", type=float, default=0.999, help="cosine-similarity bar of --probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 plain 1 GiB device-to-device elementwise copies (neg) whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figure")
@@ -172,6 +203,14 @@ def main():
         api.attn_fwd(ws, shape, params, w.causal, out)
         if ev is not None:
             ev[3].record(stream)
+
+    if args.probe:
+        if args.qk == "mxfp4" or args.pv != "fp8":
+            print("--probe compares integer Q/K codes with FP8 P~V: leave --qk and --pv at their defaults",
+                  file=sys.stderr)
+            sys.exit(2)
+        probe_bench(args, w, qt, kt, vt, shape, ws, dev)
+        return
 
     for _ in range(args.warmup):
         step()

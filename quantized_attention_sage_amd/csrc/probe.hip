@@ -9,12 +9,15 @@
 // distance against full-precision attention.
 //
 //  * exact_part_kernel: work-group (split s, head bh) runs a plain fp32 online
-//    softmax over the keys of split s for the 128 rows of the block.  Lane
-//    pairs (l, l^32) share a row, each holding half of q and of the output
-//    row; a score is the sum of the two half dot products.  K and V sub-tiles
-//    of 32 keys are staged in LDS as fp32.
-//  * exact_merge_kernel: combines the splits (max of the running maxima, then
-//    the weighted sums) into the reference rows.
+//    softmax over the keys of split s for the 128 rows of the block.  Eight
+//    lanes share four rows, each holding an eighth of q and of the four output
+//    rows, so that every K or V value read from LDS feeds four FMAs (LDS
+//    bandwidth, not the FMA rate, bounds this loop otherwise); a score is the
+//    sum of the eight partial dot products.  K and V sub-tiles of 8 keys are
+//    staged in LDS as fp32.
+//  * exact_merge_kernel: one work-group per (head, row), one lane per channel,
+//    combines the splits (max of the running maxima, then the weighted sums)
+//    into the reference rows.
 //  * probe_sums_kernel / probe_total_kernel: fp64 sums over the valid rows of
 //    every head, then over the heads in order.
 #include "sage_internal.h"
@@ -23,7 +26,7 @@ namespace sage {
 namespace {
 
 constexpr int kRows = 128;   // one query block
-constexpr int kSub = 32;     // keys per LDS sub-tile
+constexpr int kSub = 8;      // keys per LDS sub-tile
 
 template <bool BF16>
 __device__ __forceinline__ float ld16(const void* base, int64_t i) {
@@ -42,74 +45,155 @@ struct ExactArgs {
   float* part;         // [S, BH, 128, D + 2]: unnormalised row, running max, row sum
 };
 
+// 8 bf16/fp16 values (16 bytes) to fp32
+template <bool BF16>
+__device__ __forceinline__ void cvt8(uint4 u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BF16) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      f[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] & 0xffffu)));
+      f[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+    }
+  }
+}
+
+// Sum over each aligned group of 8 lanes, with DPP lane moves (no LDS
+// round trip): swap neighbours, swap pairs, then mirror within the 8.
+__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
+  const int v = __float_as_int(x);
+  int r;
+  if (ctrl_sel == 0) r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
+  else if (ctrl_sel == 1) r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  else r = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);                     // row_half_mirror
+  return __int_as_float(r);
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f(x, 0);
+  x += dpp_f(x, 1);
+  return x + dpp_f(x, 2);
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void exact_part_kernel(ExactArgs a) {
-  constexpr int DH = D / 2;
-  constexpr int RS = DH + 4;    // half-row stride in LDS: the two halves fall in different banks
-  __shared__ float ks[kSub][2][RS];
-  __shared__ float vs[kSub][2][RS];
+  constexpr int LPR = 8;          // lanes sharing a row
+  constexpr int RPL = 4;          // rows per lane: each value read from LDS feeds RPL FMAs
+  constexpr int DQ = D / LPR;     // channels per lane
+  constexpr int RS = DQ + 4;      // segment stride in LDS: the eight segments fall in different banks
+  __shared__ __attribute__((aligned(16))) float ks[kSub][LPR][RS];
+  __shared__ __attribute__((aligned(16))) float vs[kSub][LPR][RS];
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int r = 32 * w + (l & 31), half = l >> 5;
+  const int g = l / LPR, qd = l % LPR;
+  // rows of this lane: 32 w + g + 8 u, u < RPL; channels DQ qd ..
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
-  const int qi = a.q0 + r;
 
-  float q[DH];
-  {
-    const int64_t base = b * a.qs0 + h * a.qs1 + static_cast<int64_t>(min(qi, a.N - 1)) * a.qs2 + half * DH;
+  float q[RPL][DQ], o[RPL][DQ], m[RPL], lsum[RPL];
+  int qi[RPL];
 #pragma unroll
-    for (int c = 0; c < DH; ++c) q[c] = qi < a.N ? ld16<BF16>(a.q, base + c) : 0.f;
+  for (int u = 0; u < RPL; ++u) {
+    qi[u] = a.q0 + 32 * w + g + 8 * u;
+    const int64_t base = b * a.qs0 + h * a.qs1 + static_cast<int64_t>(min(qi[u], a.N - 1)) * a.qs2 + qd * DQ;
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) {
+      q[u][c] = qi[u] < a.N ? ld16<BF16>(a.q, base + c) : 0.f;
+      o[u][c] = 0.f;
+    }
+    m[u] = -INFINITY;
+    lsum[u] = 0.f;
   }
-  float o[DH];
-#pragma unroll
-  for (int c = 0; c < DH; ++c) o[c] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
 
   const int kb = split * a.chunk, ke = min(a.key_end, kb + a.chunk);
   const int64_t kbase = b * a.ks0 + h * a.ks1, vbase = b * a.vs0 + h * a.vs1;
+  constexpr int LOADS = kSub * D / 8;   // 16-byte loads per sub-tile and tensor
   for (int j0 = kb; j0 < ke; j0 += kSub) {
     __syncthreads();
-    for (int e = t; e < kSub * D; e += 256) {
-      const int jj = e / D, c = e % D, j = j0 + jj;
-      const bool in = j < ke;
-      ks[jj][c / DH][c % DH] = in ? ld16<BF16>(a.k, kbase + static_cast<int64_t>(j) * a.ks2 + c) : 0.f;
-      vs[jj][c / DH][c % DH] = in ? ld16<BF16>(a.v, vbase + static_cast<int64_t>(j) * a.vs2 + c) : 0.f;
+    if (t < LOADS) {
+      const int jj = t / (D / 8), c = 8 * (t % (D / 8)), j = j0 + jj;
+      float fk[8], fv[8];
+      if (j < ke) {
+        cvt8<BF16>(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + kbase +
+                                                   static_cast<int64_t>(j) * a.ks2 + c), fk);
+        cvt8<BF16>(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + vbase +
+                                                   static_cast<int64_t>(j) * a.vs2 + c), fv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fk[i] = fv[i] = 0.f;
+      }
+      float* kd = &ks[jj][c / DQ][c % DQ];
+      float* vd = &vs[jj][c / DQ][c % DQ];
+#pragma unroll
+      for (int i = 0; i < 8; i += 4) {
+        *reinterpret_cast<float4*>(kd + i) = make_float4(fk[i], fk[i + 1], fk[i + 2], fk[i + 3]);
+        *reinterpret_cast<float4*>(vd + i) = make_float4(fv[i], fv[i + 1], fv[i + 2], fv[i + 3]);
+      }
     }
     __syncthreads();
-    float sc[kSub];
-    float mt = -INFINITY;
+    float sc[RPL][kSub];
+    float mt[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) mt[u] = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < kSub; ++jj) {
-      float dot = 0.f;
+      float kr[DQ];
 #pragma unroll
-      for (int c = 0; c < DH; ++c) dot = fmaf(q[c], ks[jj][half][c], dot);
-      dot += __shfl_xor(dot, 32);
+      for (int c = 0; c < DQ; ++c) kr[c] = ks[jj][qd][c];
       const int j = j0 + jj;
-      const bool vis = j < ke && (!a.causal || j <= qi);
-      sc[jj] = vis ? dot * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sc[jj]);
-    }
-    const float mn = fmaxf(m, mt);
-    if (mn == -INFINITY) continue;   // no visible key for this row yet
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 while m is -inf
-    lsum *= alpha;
+      float dot[RPL];
 #pragma unroll
-    for (int c = 0; c < DH; ++c) o[c] *= alpha;
+      for (int u = 0; u < RPL; ++u) dot[u] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DQ; ++c)     // rows innermost: RPL independent FMA chains
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) dot[u] = fmaf(q[u][c], kr[c], dot[u]);
+#pragma unroll
+      for (int u = 0; u < RPL; ++u) {
+        const float d8 = sum8(dot[u]);
+        const bool vis = j < ke && (!a.causal || j <= qi[u]);
+        sc[u][jj] = vis ? d8 * a.scale_log2 : -INFINITY;
+        mt[u] = fmaxf(mt[u], sc[u][jj]);
+      }
+    }
+    float mn[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      mn[u] = fmaxf(m[u], mt[u]);
+      // alpha = 0 while m is -inf; a row with no visible key yet keeps m = -inf, o = 0, l = 0
+      const float alpha = mn[u] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[u] - mn[u]);
+      lsum[u] *= alpha;
+#pragma unroll
+      for (int c = 0; c < DQ; ++c) o[u][c] *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < kSub; ++jj)
+        sc[u][jj] = mn[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[u][jj] - mn[u]);
+      m[u] = mn[u];
+    }
 #pragma unroll
     for (int jj = 0; jj < kSub; ++jj) {
-      const float p = __builtin_amdgcn_exp2f(sc[jj] - mn);
-      lsum += p;
+      float vr[DQ];
 #pragma unroll
-      for (int c = 0; c < DH; ++c) o[c] = fmaf(p, vs[jj][half][c], o[c]);
+      for (int c = 0; c < DQ; ++c) vr[c] = vs[jj][qd][c];
+#pragma unroll
+      for (int u = 0; u < RPL; ++u) {
+        lsum[u] += sc[u][jj];
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) o[u][c] = fmaf(sc[u][jj], vr[c], o[u][c]);
+      }
     }
-    m = mn;
   }
-  float* dst = a.part + ((static_cast<int64_t>(split) * gridDim.y + bh) * kRows + r) * (D + 2);
 #pragma unroll
-  for (int c = 0; c < DH; ++c) dst[half * DH + c] = o[c];
-  if (half == 0) {
-    dst[D] = m;
-    dst[D + 1] = lsum;
+  for (int u = 0; u < RPL; ++u) {
+    const int r = 32 * w + g + 8 * u;
+    float* dst = a.part + ((static_cast<int64_t>(split) * gridDim.y + bh) * kRows + r) * (D + 2);
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) dst[qd * DQ + c] = o[u][c];
+    if (qd == 0) {
+      dst[D] = m[u];
+      dst[D + 1] = lsum[u];
+    }
   }
 }
 
@@ -120,22 +204,21 @@ struct MergeArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void exact_merge_kernel(MergeArgs a) {
-  const int bh = blockIdx.x;
-  for (int e = threadIdx.x; e < kRows * D; e += 256) {
-    const int r = e / D, c = e % D;
-    float mx = -INFINITY;
-    for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.part[((static_cast<int64_t>(s) * a.BH + bh) * kRows + r) * (D + 2) + D]);
-    float lt = 0.f, ot = 0.f;
-    for (int s = 0; s < a.S; ++s) {
-      const float* p = a.part + ((static_cast<int64_t>(s) * a.BH + bh) * kRows + r) * (D + 2);
-      if (p[D] == -INFINITY) continue;
-      const float wgt = __builtin_amdgcn_exp2f(p[D] - mx);
-      lt = fmaf(wgt, p[D + 1], lt);
-      ot = fmaf(wgt, p[c], ot);
-    }
-    a.ref[(static_cast<int64_t>(bh) * kRows + r) * D + c] = (a.q0 + r < a.N && lt > 0.f) ? ot / lt : 0.f;
+__global__ __launch_bounds__(D) void exact_merge_kernel(MergeArgs a) {
+  const int bh = blockIdx.x, r = blockIdx.y, c = threadIdx.x;
+  const float* row0 = a.part + (static_cast<int64_t>(bh) * kRows + r) * (D + 2);
+  const int64_t split_stride = static_cast<int64_t>(a.BH) * kRows * (D + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, row0[s * split_stride + D]);
+  float lt = 0.f, ot = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float* p = row0 + s * split_stride;
+    if (p[D] == -INFINITY) continue;
+    const float wgt = __builtin_amdgcn_exp2f(p[D] - mx);
+    lt = fmaf(wgt, p[D + 1], lt);
+    ot = fmaf(wgt, p[c], ot);
   }
+  a.ref[(static_cast<int64_t>(bh) * kRows + r) * D + c] = (a.q0 + r < a.N && lt > 0.f) ? ot / lt : 0.f;
 }
 
 struct SumArgs {
@@ -233,8 +316,8 @@ hipError_t launch_probe_reference(const Problem& p, TensorView q, TensorView k, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs mg{a.part, reinterpret_cast<float*>(scratch + L.ref), L.splits, BH, a.q0, p.N};
-  if (p.D == 128) hipLaunchKernelGGL((exact_merge_kernel<128>), dim3(BH), dim3(256), 0, st, mg);
-  else hipLaunchKernelGGL((exact_merge_kernel<64>), dim3(BH), dim3(256), 0, st, mg);
+  if (p.D == 128) hipLaunchKernelGGL((exact_merge_kernel<128>), dim3(BH, kRows), dim3(128), 0, st, mg);
+  else hipLaunchKernelGGL((exact_merge_kernel<64>), dim3(BH, kRows), dim3(64), 0, st, mg);
   return hipGetLastError();
 }
 

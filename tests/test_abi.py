@@ -175,7 +175,7 @@ def test_entry_points_validate_before_launching():
 
 def test_probe_scratch_bytes():
     """Exact rows fp32, two outputs of the I/O type, per-split partial rows
-    (at most 64 splits of whole 32-key sub-tiles, 1024 keys up to 64K keys)
+    (at most 64 splits of whole 8-key sub-tiles, 1024 keys up to 64K keys)
     and the fp64 sums, each span 256-byte aligned."""
     def al(x):
         return (x + 255) // 256 * 256
@@ -183,7 +183,7 @@ def test_probe_scratch_bytes():
         n = ctypes.c_size_t()
         assert L.lib().sage_probe_scratch_bytes(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(n)) == L.SAGE_OK
         BH, n_pad = B * H, (N + 127) // 128 * 128
-        chunk = 1024 if n_pad <= 64 * 1024 else ((n_pad + 63) // 64 + 31) // 32 * 32
+        chunk = 1024 if n_pad <= 64 * 1024 else ((n_pad + 63) // 64 + 7) // 8 * 8
         S = -(-n_pad // chunk)
         assert S <= 64
         want = al(BH * 128 * d * 4) + 2 * al(BH * 128 * d * 2) + al(S * BH * 128 * (d + 2) * 4) + al(BH * 64) + al(64)
