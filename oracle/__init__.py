@@ -21,6 +21,8 @@ Two parts, each citing the passage of the pages it follows:
   abstract, read as a probe of one sampled query block per head.
 * ``fp4`` -- MXFP4 (E2M1 codes with E8M0 scales per 32 channels) for the FP4
   microscaling of the SageAttention3 abstract.
+* ``fp6`` -- E2M3 and the slot packing that holds INT4-range codes for an
+  FP6 matrix product.
 * ``fp8`` -- the OCP E4M3 ("fn") format, decoded from its definition and
   encoded by nearest-value search with ties to the even code.
 
@@ -31,7 +33,7 @@ emulation with the papers' own kernels is "parity unpinned"; what is pinned is
 agreement with exact attention when quantisation is switched off, the
 quantiser invariants, the codec, and the reduction order.
 """
-from . import fp4, fp8, reduce, quant, attention, metrics, adaptive  # noqa: F401
+from . import fp4, fp6, fp8, reduce, quant, attention, metrics, adaptive  # noqa: F401
 
 from .fp8 import e4m3_decode, e4m3_encode  # noqa: F401
 from .reduce import canonical_sum, canonical_mean, pad_length  # noqa: F401

@@ -48,6 +48,7 @@ import math
 
 import numpy as np
 
+from .fp6 import e2m3_decode, unpack_slots
 from .fp8 import e4m3_decode, e4m3_encode
 from .quant import QBLOCK, q_group_index, k_group_index, bias_row
 
@@ -134,6 +135,10 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
                 # integer codes held as E4M3 bytes: decode to the same integers
                 qmat = e4m3_decode(qk["q_codes"][b, h, q0:q0 + QBLOCK])
                 kmat = e4m3_decode(qk["k_codes"][b, h])
+            elif qk.get("qk_format", "int") == "int_e2m3":
+                # integer codes held as packed E2M3: unpack and decode to the same integers
+                qmat = e2m3_decode(unpack_slots(qk["q_codes"][b, h, q0:q0 + QBLOCK]))
+                kmat = e2m3_decode(unpack_slots(qk["k_codes"][b, h]))
             else:
                 qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
                 kmat = qk["k_codes"][b, h].astype(np.float64)

@@ -23,7 +23,9 @@ Readings where the pages are silent (each one is listed in the design doc):
     of every mean and amax.
   * qk_format "int_e4m3" stores the INT4-range integer codes as the E4M3 byte
     of the same integer (exact for |code| <= 15; code 0 is byte 0): the same
-    numbers in the operand format of an FP8 matrix product.
+    numbers in the operand format of an FP8 matrix product.  "int_e2m3" holds
+    them as 6-bit E2M3 codes (exact for |code| <= 7) packed in the operand
+    layout of an FP6 matrix product (oracle/fp6.py).
 All arithmetic that feeds a code is numpy float32 (IEEE, round to nearest even,
 no fused multiply-add).
 """
@@ -34,6 +36,7 @@ import dataclasses
 import numpy as np
 
 from .fp4 import mx_quantize_rows, mx_decode_rows, pack_nibbles
+from .fp6 import e2m3_encode, pack_slots
 from .fp8 import e4m3_encode
 from .reduce import canonical_mean, pad_length
 
@@ -51,8 +54,8 @@ class QuantParams:
     p_range: float = 448.0
     v_range: float = 448.0
     pv: str = "fp8"          # P~V precision: "fp8" (SageAttention2), or "bf16" / "fp16" (SageAttention)
-    qk_format: str = "int"   # "int" (INT8 / INT4-range, qk_bits and gran), "int_e4m3" (INT4-range held
-                             # as E4M3 bytes) or "mxfp4" (SageAttention3's FP4)
+    qk_format: str = "int"   # "int" (INT8 / INT4-range, qk_bits and gran), "int_e4m3" / "int_e2m3"
+                             # (INT4-range held as E4M3 bytes / packed E2M3) or "mxfp4" (SageAttention3's FP4)
 
     @property
     def qmax(self) -> int:
@@ -137,10 +140,10 @@ def quant_qk(q: np.ndarray, k: np.ndarray, p: QuantParams = QuantParams(), with_
     n_pad = n_padded(N)
     valid = np.arange(n_pad) < N
     mx = p.qk_format == "mxfp4"
-    if p.qk_format not in ("int", "mxfp4", "int_e4m3"):
-        raise ValueError("qk_format must be int, int_e4m3 or mxfp4")
-    if p.qk_format == "int_e4m3" and p.qk_bits != 4:
-        raise ValueError("int_e4m3 holds INT4-range codes: qk_bits must be 4")
+    if p.qk_format not in ("int", "mxfp4", "int_e4m3", "int_e2m3"):
+        raise ValueError("qk_format must be int, int_e4m3, int_e2m3 or mxfp4")
+    if p.qk_format in ("int_e4m3", "int_e2m3") and p.qk_bits != 4:
+        raise ValueError(f"{p.qk_format} holds INT4-range codes: qk_bits must be 4")
     qmax = None if mx else p.qmax
     qp = _pad_tokens(q, n_pad)
     kp = _pad_tokens(k, n_pad)
@@ -184,6 +187,9 @@ def quant_qk(q: np.ndarray, k: np.ndarray, p: QuantParams = QuantParams(), with_
     elif p.qk_format == "int_e4m3":
         out["q_codes"] = e4m3_encode(q_codes.astype(np.float32))
         out["k_codes"] = e4m3_encode(k_codes.astype(np.float32))
+    elif p.qk_format == "int_e2m3":
+        out["q_codes"] = pack_slots(e2m3_encode(q_codes.astype(np.float32)))
+        out["k_codes"] = pack_slots(e2m3_encode(k_codes.astype(np.float32)))
     if with_bias:
         out["bias"] = np.stack([[np.stack([bias_row(out, b, h, qb) for qb in range(nqb)])
                                  for h in range(H)] for b in range(B)])
