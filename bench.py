@@ -28,7 +28,7 @@ PEAK_BF16_TOPS = 2500.0 # MI355X dense bf16 / fp16 matrix peak
 # With the 16-bit P~V half of the work (QK^T) runs at the INT8 rate and half
 # (P~V) at the bf16 rate: the path's peak is 2 / (1/5000 + 1/2500) TOPS.
 PEAK_PV16_TOPS = 2.0 / (1.0 / PEAK_TOPS + 1.0 / PEAK_BF16_TOPS)
-PEAK_FP4_TOPS = 10100.0 # MI355X dense FP4 matrix peak
+PEAK_FP4_TOPS = 10100.0 # MI355X dense FP4 and FP6 matrix peak
 # With MXFP4 Q and K, QK^T runs at the FP4 rate and P~V at the FP8 one.
 PEAK_MXFP4_TOPS = 2.0 / (1.0 / PEAK_FP4_TOPS + 1.0 / PEAK_TOPS)
 HBM_PEAK_GBS = 8000.0
@@ -151,10 +151,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--qk", choices=("int", "int_e4m3", "mxfp4"), default="int",
-                    help="Q/K codes: int (INT8 / INT4-range per the workload, the default), int_e4m3 "
-                         "(the INT4-range codes held as E4M3 bytes on the FP8 matrix cores; INT4-range "
-                         "workloads only) or mxfp4 (FP4 E2M1 with an E8M0 scale per 32 channels)")
+    ap.add_argument("--qk", choices=("int", "int_e4m3", "int_e2m3", "mxfp4"), default="int",
+                    help="Q/K codes: int (INT8 / INT4-range per the workload, the default), int_e4m3 / "
+                         "int_e2m3 (the INT4-range codes held as E4M3 bytes / packed FP6 E2M3 on the FP8 / FP6 "
+                         "matrix cores; INT4-range workloads only) or mxfp4 (FP4 E2M1 with an E8M0 scale per "
+                         "32 channels)")
     ap.add_argument("--pv", choices=("fp8", "f16"), default="fp8",
                     help="P~V precision: fp8 (SageAttention2, the default) or f16 (16-bit P~ and V, "
                          "the first SageAttention's setting)")
@@ -177,8 +178,8 @@ def main():
     from quantized_attention_sage_amd.workloads import WORKLOADS, make_inputs, describe
 
     w = WORKLOADS[args.workload]
-    if args.qk == "int_e4m3" and w.qk_bits != 4:
-        print(f"--qk int_e4m3 holds INT4-range codes; workload {w.name} uses INT{w.qk_bits}", file=sys.stderr)
+    if args.qk in ("int_e4m3", "int_e2m3") and w.qk_bits != 4:
+        print(f"--qk {args.qk} holds INT4-range codes; workload {w.name} uses INT{w.qk_bits}", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
@@ -241,8 +242,10 @@ def main():
     tops = w.ops / (ms_per_step * 1e-3) / 1e12
     attn_tops = w.ops / (attn_ms * 1e-3) / 1e12
     pv16, mx = args.pv == "f16", args.qk == "mxfp4"
-    peak = PEAK_PV16_TOPS if pv16 else (PEAK_MXFP4_TOPS if mx else PEAK_TOPS)
-    traffic = None if (pv16 or mx or args.qk == "int_e4m3") else traffic_from_profile(w.name)
+    # FP4 and FP6 share the 10.1 P/s dense rate: the E2M3-held codes are priced like MXFP4 (QK at that rate,
+    # P~V at the FP8 rate, half the operations each)
+    peak = PEAK_PV16_TOPS if pv16 else (PEAK_MXFP4_TOPS if (mx or args.qk == "int_e2m3") else PEAK_TOPS)
+    traffic = None if (pv16 or mx or args.qk != "int") else traffic_from_profile(w.name)
     qk_bytes, v_bytes = quant_bytes(w, args.pv, args.qk)
     rec = {
         "metric": "attention TOPS (4*B*H*N^2*d, halved if causal) of quant_qk + quant_v + attn_fwd",
@@ -256,11 +259,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": (("mxfp4 QK" if mx else ("int8 QK" if w.qk_bits == 8 else
-                                          ("int4-range QK as e4m3" if args.qk == "int_e4m3" else "int4-range QK"))) +
+                                          ("int4-range QK as " + args.qk[4:] if args.qk != "int" else "int4-range QK"))) +
                   (f" / {w.dtype} PV" if pv16 else " / fp8 PV") + f" ({w.dtype} in/out)"),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "io_dtype": w.dtype, "qk": "mxfp4" if mx else f"int{w.qk_bits}" + ("_e4m3" if args.qk == "int_e4m3" else ""),
+                   "io_dtype": w.dtype, "qk": "mxfp4" if mx else f"int{w.qk_bits}" + (args.qk[3:] if args.qk != "int" else ""),
                    "granularity": w.gran,
                    "pv": args.pv},
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 1), "peak": round(peak, 1), "unit": "TFLOP/s",

@@ -10,8 +10,9 @@
  *   Q' = Q - mean_block(Q)                        (per channel, per 128-token block qb)
  *   dS[qb, j] = mean_block(Q)(qb) . K'_j          (restores the Q mean)
  *   Q', K'  -> integer codes with per-group scales (INT8, or INT4-range [-7,7]
- *              held in int8 on the INT8 matrix cores or, with SAGE_QK_INT_E4M3,
- *              held as E4M3 bytes on the FP8 matrix cores, with the same S)
+ *              held in int8 on the INT8 matrix cores or, with SAGE_QK_INT_E4M3
+ *              / _E2M3, held as E4M3 / FP6 E2M3 on the FP8 / FP6 matrix cores,
+ *              with the same S)
  *   V'  = V - mean_tokens(V); V' -> FP8 E4M3 with per-channel scales
  *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles against a
  *         reference maximum m that moves only when a tile's row maximum exceeds
@@ -45,7 +46,7 @@ extern "C" {
 #define SAGE_API __attribute__((visibility("default")))
 
 /* Bumped whenever a buffer layout, a group map or a struct below changes. */
-#define SAGE_ABI_VERSION 4
+#define SAGE_ABI_VERSION 5
 
 typedef enum {
   SAGE_OK = 0,
@@ -92,8 +93,20 @@ typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_F16 = 1 } sage_pv_mode;
  *                  the FP8 matrix cores with fp32 accumulation; every partial
  *                  sum is an integer below 2^24, so S is bit-identical to the
  *                  integer product of SAGE_QK_INT and so is the output.  With
- *                  SAGE_PV_FP8 only. */
-typedef enum { SAGE_QK_INT = 0, SAGE_QK_MXFP4 = 1, SAGE_QK_INT_E4M3 = 2 } sage_qk_format;
+ *                  SAGE_PV_FP8 only.
+ *   SAGE_QK_INT_E2M3: the same INT4-range codes as 6-bit FP6 E2M3 codes (every
+ *                  integer in [-7, 7] is exact; sign bit 5, exponent bits 4:3
+ *                  with bias 1, mantissa bits 2:0), packed in the operand
+ *                  layout of the 64-deep FP6 matrix product, which runs at
+ *                  twice the FP8 rate.  Per token and per 64-channel group j,
+ *                  half h (h in {0, 1}) is a slot of 32 values: value i is
+ *                  channel 64j + 16h + i for i < 16 and 64j + 32 + 16h + i - 16
+ *                  for i >= 16, at bits 6i .. 6i + 5 of 24 bytes.  The slot's
+ *                  bytes 0..15 sit at byte 16(4j + h) of the token's d bytes,
+ *                  bytes 16..23 at byte 16(4j + 2 + h), followed by 8 zero
+ *                  bytes.  S and the output are bit-identical to SAGE_QK_INT.
+ *                  qk_bits must be 4; SAGE_PV_FP8 only. */
+typedef enum { SAGE_QK_INT = 0, SAGE_QK_MXFP4 = 1, SAGE_QK_INT_E4M3 = 2, SAGE_QK_INT_E2M3 = 3 } sage_qk_format;
 
 /* Shape of Q, K, V ([B, H, N, d], element type dtype).  Strides are in
  * elements for the B, H and N dimensions; the d dimension is contiguous.
@@ -132,7 +145,8 @@ typedef struct {
  *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j] * sm_scale * log2(e)
  *            (the bias in the exp2 domain of the softmax); 0 for j >= N
  *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)
- * With SAGE_QK_INT_E4M3 q_codes and k_codes hold E4M3 bytes (same layout).
+ * With SAGE_QK_INT_E4M3 q_codes and k_codes hold E4M3 bytes (same layout);
+ * with SAGE_QK_INT_E2M3 each d-byte row holds the packed E2M3 slots.
  * With SAGE_QK_MXFP4 the codes and scales of Q and K are instead
  *   q_codes, k_codes  uint8 [B, H, N_pad, d/2]   E2M1 codes, channel 2i in the
  *                     low nibble of byte i; rows >= N hold 0
@@ -249,7 +263,8 @@ SAGE_API sage_status sage_probe_scratch_bytes(const sage_shape* s, size_t* bytes
  * 128 q_block .. 128 q_block + 127 that are < N) of every head it
  *   1. runs sage_quant_v, then the method with INT8 codes (qk_format
  *      SAGE_QK_INT) and with INT4-range codes (qk_bits 4, in p->qk_format:
- *      SAGE_QK_INT or SAGE_QK_INT_E4M3), keeping both outputs in the I/O type;
+ *      SAGE_QK_INT, _INT_E4M3 or _INT_E2M3), keeping both outputs in the I/O
+ *      type;
  *   2. computes exact attention of the same rows in fp32 (fp32 dot products
  *      and online softmax, no quantisation, no smoothing);
  *   3. forms cosine similarity and relative L1 of each output against it over

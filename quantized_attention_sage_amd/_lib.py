@@ -16,8 +16,8 @@ SAGE_OK, SAGE_EINVAL, SAGE_EUNSUPPORTED, SAGE_EHIP = 0, 1, 2, 3
 SAGE_F16, SAGE_BF16 = 0, 1
 GRAN = {"thread": 0, "warp": 1, "block": 2}
 PV_MODE = {"fp8": 0, "f16": 1}
-QK_FORMAT = {"int": 0, "mxfp4": 1, "int_e4m3": 2}
-ABI_VERSION = 4
+QK_FORMAT = {"int": 0, "mxfp4": 1, "int_e4m3": 2, "int_e2m3": 3}
+ABI_VERSION = 5
 
 c_i64_3 = ctypes.c_int64 * 3
 

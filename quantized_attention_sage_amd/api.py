@@ -63,7 +63,7 @@ class Workspace:
         self.shape = (shape.B, shape.H, shape.N, shape.d)
         self.pv_f16 = params.pv_mode == L.PV_MODE["f16"]
         self.qk_mx = params.qk_format == L.QK_FORMAT["mxfp4"]
-        self.qk_e4m3 = params.qk_format == L.QK_FORMAT["int_e4m3"]
+        self.qk_held = params.qk_format in (L.QK_FORMAT["int_e4m3"], L.QK_FORMAT["int_e2m3"])
         self.tensor = torch.empty(lay.total_bytes + 256, dtype=torch.uint8, device=device)
         base = self.tensor.data_ptr()
         self._pad = (-base) % 256
@@ -87,7 +87,7 @@ class Workspace:
         lay = self.layout
         n_pad, nblk = lay.n_pad, lay.n_qblocks
         sp = getattr(lay, name)
-        code_t = torch.uint8 if self.qk_e4m3 else torch.int8     # E4M3 bytes or int8 codes
+        code_t = torch.uint8 if self.qk_held else torch.int8     # E4M3 / packed E2M3 bytes, or int8 codes
         raw = self.tensor[self._pad + sp.offset: self._pad + sp.offset + sp.bytes]
         shapes = {
             "q_codes": (torch.uint8, (B, H, n_pad, d // 2)) if self.qk_mx else (code_t, (B, H, n_pad, d)),

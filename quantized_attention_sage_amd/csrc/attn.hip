@@ -34,6 +34,7 @@
 namespace sage {
 namespace {
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -190,10 +191,6 @@ __device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, int k0
   }
 }
 
-// F8QK: Q and K codes are small integers held as E4M3 bytes, multiplied on
-// v_mfma_f32_32x32x64_f8f6f4 (two 32-channel fragments per instruction).  Every
-// product and partial sum is an integer below 2^24, so the fp32 result equals
-// the integer product exactly and the int->float conversion disappears.
 // The same copy with the K scales spread so that subtile st, lane half h
 // reads entry 2 st + h for every granularity (64-key groups: entry j holds
 // group j / 4).  s_src is wave 2's per-lane source offset.
@@ -205,10 +202,24 @@ __device__ __forceinline__ void copy_aux_spread(uint32_t slot, const TileSrc& s,
   }
 }
 
+// 24 bytes of FP6 codes as an 8-register MFMA operand (the top two registers unused).
+__device__ __forceinline__ i32x8 cat6(i32x4 a, i32x2 b) {
+  const i32x4 bw = __builtin_shufflevector(b, b, 0, 1, -1, -1);
+  return __builtin_shufflevector(a, bw, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+
+// QKF: how the Q and K codes are held.  0: int8 on v_mfma_i32_32x32x32_i8.
+// 1 (E4M3) and 2 (packed FP6 E2M3): small integers in a float format on
+// v_mfma_f32_32x32x64_f8f6f4, 64 channels per instruction (FP6 at twice the FP8
+// rate).  Every product and partial sum is an integer below 2^24, so the fp32
+// result equals the integer product exactly and the int->float conversion
+// disappears.
 // PROBE: one work-group per head, on query block a.probe_qb only.
-template <int D, bool BF16, bool F8QK, bool PROBE>
+template <int D, bool BF16, int QKF, bool PROBE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // 32-channel fragments of Q^ and K^ per row
+  constexpr bool F8QK = QKF != 0;          // a float-format QK product (E4M3 or E2M3)
+  constexpr int CBSZ = QKF == 2 ? 2 : 0;    // operand format of that product: FP8 E4M3, or FP6 E2M3
   constexpr int KSF = F8QK ? KS / 2 : KS;  // QK MFMAs per 32-key subtile
   constexpr int CT = D / 32;          // 32-channel tiles of the output
   constexpr int NQK = 4 * KSF;        // QK MFMAs per tile
@@ -241,16 +252,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const float* kscale = a.k_scale + static_cast<int64_t>(bh) * n_kscale;
 
   i32x4 qf[KS];
-  i32x8 qf8[KSF];   // F8QK: fragments 2j, 2j+1 as one operand
+  i32x8 qf8[KSF];   // F8QK: fragments 2j, 2j+1 as one operand (E2M3: 16 + 8 bytes of a 24-byte slot)
   {
     const int8_t* qrow = a.q_codes + (static_cast<int64_t>(bh) * a.n_pad + qi) * D;
     if constexpr (F8QK) {
 #pragma unroll
       for (int j = 0; j < KSF; ++j) {
         const i32x4 a0 = *reinterpret_cast<const i32x4*>(qrow + 64 * j + 16 * hh);
-        const i32x4 a1 = *reinterpret_cast<const i32x4*>(qrow + 64 * j + 32 + 16 * hh);
-        qf8[j][0] = a0[0]; qf8[j][1] = a0[1]; qf8[j][2] = a0[2]; qf8[j][3] = a0[3];
-        qf8[j][4] = a1[0]; qf8[j][5] = a1[1]; qf8[j][6] = a1[2]; qf8[j][7] = a1[3];
+        if constexpr (QKF == 2) {
+          const i32x2 a1 = *reinterpret_cast<const i32x2*>(qrow + 64 * j + 32 + 16 * hh);
+          qf8[j] = cat6(a0, a1);
+        } else {
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(qrow + 64 * j + 32 + 16 * hh);
+          qf8[j][0] = a0[0]; qf8[j][1] = a0[1]; qf8[j][2] = a0[2]; qf8[j][3] = a0[3];
+          qf8[j][4] = a1[0]; qf8[j][5] = a1[1]; qf8[j][6] = a1[2]; qf8[j][7] = a1[3];
+        }
       }
     } else {
 #pragma unroll
@@ -318,13 +334,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     return lds_i4(ko[kk] + slot_off + 32 * st * D);
   };
   // F8QK: channels 64j.. of a key as one 32-byte operand (fragments 2j, 2j+1)
+  // (E2M3: the 24-byte slot, 16 bytes of fragment 2j and the first 8 of 2j+1)
   auto k_frag2 = [&](const uint32_t* ko, int slot_off, int st, int j) __attribute__((always_inline)) {
     const i32x4 a0 = lds_i4(ko[2 * j] + slot_off + 32 * st * D);
-    const i32x4 a1 = lds_i4(ko[2 * j + 1] + slot_off + 32 * st * D);
-    i32x8 r;
-    r[0] = a0[0]; r[1] = a0[1]; r[2] = a0[2]; r[3] = a0[3];
-    r[4] = a1[0]; r[5] = a1[1]; r[6] = a1[2]; r[7] = a1[3];
-    return r;
+    if constexpr (QKF == 2) {
+      return cat6(a0, *reinterpret_cast<const i32x2*>(lds + ko[2 * j + 1] + slot_off + 32 * st * D));
+    } else {
+      const i32x4 a1 = lds_i4(ko[2 * j + 1] + slot_off + 32 * st * D);
+      i32x8 r;
+      r[0] = a0[0]; r[1] = a0[1]; r[2] = a0[2]; r[3] = a0[3];
+      r[4] = a1[0]; r[5] = a1[1]; r[6] = a1[2]; r[7] = a1[3];
+      return r;
+    }
   };
   auto v_frag = [&](const uint32_t (*vo)[2], int slot_off, int kc, int c) __attribute__((always_inline)) {
     const i32x4 v0 = lds_i4(vo[kc][0] + slot_off + 32 * c * kTile);
@@ -357,8 +378,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     if constexpr (F8QK) {
 #pragma unroll
       for (int j = 0; j < KSF; ++j)
-        sA[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_frag2(kofl, R::K0, st, j), qf2(j), sA[st], 0, 0, 0,
-                                                                 0, 0, 0);
+        sA[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_frag2(kofl, R::K0, st, j), qf2(j), sA[st], CBSZ,
+                                                                 CBSZ, 0, 0, 0, 0);
     } else {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
@@ -524,7 +545,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         if constexpr (F8QK) {
           const int sn = e / KSF, j = e % KSF;
           S_nxt[sn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf2[e & 1], qf2(j), j == 0 ? zero16 : S_nxt[sn],
-                                                                      0, 0, 0, 0, 0, 0);
+                                                                      CBSZ, CBSZ, 0, 0, 0, 0);
         } else {
           const int sn = e / KS, kk = e % KS;
           S_nxt[sn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[e % 3], qf[kk], kk == 0 ? zero16 : S_nxt[sn], 0, 0, 0);
@@ -590,7 +611,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool BF16, bool F8QK>
+template <int D, bool BF16, int QKF>
 hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal, void* o,
                      const int64_t o_stride[3], hipStream_t st, int probe_qb) {
   AttnArgs a;
@@ -602,8 +623,8 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.log2_pr = log2f(p.p_range);
   a.probe_qb = probe_qb;
   const int grid = probe_qb >= 0 ? p.B * p.H : p.nblk * p.B * p.H;
-  if (probe_qb >= 0) hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, F8QK, true>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, F8QK, false>), dim3(grid), dim3(256), 0, st, a);
+  if (probe_qb >= 0) hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, QKF, true>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, QKF, false>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -611,16 +632,22 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
 
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb) {
-  if (p.qk_e4m3) {
-    if (p.D == 128) return p.bf16 ? attn_impl<128, true, true>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                                  : attn_impl<128, false, true>(p, qk, vb, causal, o, o_stride, st, probe_qb);
-    return p.bf16 ? attn_impl<64, true, true>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                  : attn_impl<64, false, true>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+  if (p.qk_held == 2) {
+    if (p.D == 128) return p.bf16 ? attn_impl<128, true, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                                  : attn_impl<128, false, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+    return p.bf16 ? attn_impl<64, true, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                  : attn_impl<64, false, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb);
   }
-  if (p.D == 128) return p.bf16 ? attn_impl<128, true, false>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                                : attn_impl<128, false, false>(p, qk, vb, causal, o, o_stride, st, probe_qb);
-  return p.bf16 ? attn_impl<64, true, false>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                : attn_impl<64, false, false>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+  if (p.qk_held == 1) {
+    if (p.D == 128) return p.bf16 ? attn_impl<128, true, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                                  : attn_impl<128, false, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+    return p.bf16 ? attn_impl<64, true, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                  : attn_impl<64, false, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+  }
+  if (p.D == 128) return p.bf16 ? attn_impl<128, true, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                                : attn_impl<128, false, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+  return p.bf16 ? attn_impl<64, true, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb)
+                : attn_impl<64, false, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb);
 }
 
 }  // namespace sage

@@ -117,7 +117,7 @@ __host__ __device__ __forceinline__ int k_groups_per_block(int gran) { return gr
 // gmax: 128 unsigned in LDS.  Writes the block's codes (N_pad rows, so padded
 // rows get 0) and its group scales.
 template <int D, bool IS_Q>
-__device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8], int gran, int qmax, bool e4m3,
+__device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8], int gran, int qmax, int held,
                                                unsigned* gmax, int8_t* __restrict__ codes_blk,
                                                float* __restrict__ scale_blk) {
   constexpr int TOK = Tile<D>::TOK, TPR = Tile<D>::TPR;
@@ -148,7 +148,46 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
     // code = clamp(rint(x' * inv)) as an exact small integer in fp32, then its
     // low byte; four bytes per word, assembled with byte permutes.
     uint32_t packed[2];
-    if (e4m3) {
+    if (held == 2) {
+      // The same integer codes as 6-bit FP6 E2M3 codes (exact for |code| <= 7),
+      // packed into the slot layout of the 64-deep FP6 matrix product: slot
+      // (group j, half h) holds channels 64j + 16h + i (i < 16) and
+      // 64j + 32 + 16h + i - 16 (i >= 16), value i at bits 6i..6i+5 of 24
+      // bytes; the slot's bytes 0..15 sit at row byte 16(4j + h), bytes
+      // 16..23 at 16(4j + 2 + h), followed by 8 zero bytes.
+      uint32_t c24[2];
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        uint32_t mag = 0u, sgn = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = __builtin_amdgcn_fmed3f(rintf(xs[u][e + 4 * hq] * inv), -qm, qm);
+          mag |= static_cast<uint32_t>(fabsf(f)) << (8 * e);
+          sgn |= (f < 0.f ? 0x20u : 0u) << (8 * e);
+        }
+        // E2M3 codes of 0..7: 0, 8, 16, 20, 24, 26, 28, 30 (one byte each)
+        const uint32_t c = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, mag) | sgn;
+        c24[hq] = (c & 0x3Fu) | (((c >> 8) & 0x3Fu) << 6) | (((c >> 16) & 0x3Fu) << 12) | (((c >> 24) & 0x3Fu) << 18);
+      }
+      // 48 bits of this thread's 8 channels: bytes b0..b5.  Slot (j, h) comes
+      // from the threads 8j + 2h + {0, 1, 4, 5} of the row (slot bytes 0, 6,
+      // 12, 18); the first and the third of them gather their neighbours'
+      // bytes and write one 16-byte unit each.
+      const uint32_t lo4 = c24[0] | (c24[1] << 24);
+      const uint32_t hi2 = c24[1] >> 8;
+      const uint32_t lo_1 = __shfl_down(lo4, 1), hi_1 = __shfl_down(hi2, 1), lo_4 = __shfl_down(lo4, 4);
+      const int j = cg / 8, m = cg % 8;
+      uint8_t* row = reinterpret_cast<uint8_t*>(codes_blk) + static_cast<int64_t>(r) * D;
+      if (m == 0 || m == 2) {          // slot bytes 0..15 -> unit 4j + h
+        *reinterpret_cast<uint4*>(row + 16 * (4 * j + m / 2)) =
+            make_uint4(lo4, (hi2 & 0xffffu) | (lo_1 << 16), (lo_1 >> 16) | (hi_1 << 16), lo_4);
+      } else if (m == 4 || m == 6) {   // slot bytes 16..23 and 8 zero bytes -> unit 4j + 2 + h
+        *reinterpret_cast<uint4*>(row + 16 * (4 * j + 2 + (m - 4) / 2)) =
+            make_uint4((hi2 & 0xffffu) | (lo_1 << 16), (lo_1 >> 16) | (hi_1 << 16), 0u, 0u);
+      }
+      continue;
+    }
+    if (held == 1) {
       // The same integer codes held as E4M3 bytes (exact for |code| <= 15);
       // adding +0 turns -0 into +0, so that code 0 is byte 0.
       float cf[8];
@@ -222,7 +261,7 @@ struct QKArgs {
   int64_t qsB, qsH, qsN, ksB, ksH, ksN;
   sage_qk_buffers out;
   int H, N, n_pad, nblk, gran, qmax, smooth_q, smooth_k;
-  int e4m3;   // integer codes written as E4M3 bytes (INT4-range only)
+  int held;   // INT4-range integer codes written as 1: E4M3 bytes, 2: packed FP6 E2M3 (0: int8)
   float scale_log2;  // sm_scale * log2(e): the bias is stored in the exp2 domain
 };
 
@@ -277,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
                          reinterpret_cast<uint8_t*>(a.out.q_scale) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 32));
   } else {
     const int ngq = q_groups_per_block(a.gran);
-    quantize_block<D, true>(x, a.gran, a.qmax, a.e4m3, gmax, a.out.q_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+    quantize_block<D, true>(x, a.gran, a.qmax, a.held, gmax, a.out.q_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
                             a.out.q_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngq);
   }
 }
@@ -424,7 +463,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                            reinterpret_cast<uint8_t*>(a.out.k_scale) + (static_cast<int64_t>(bh) * a.n_pad + row0) * (D / 32));
     } else {
       const int ngk = k_groups_per_block(a.gran);
-      quantize_block<D, false>(x, a.gran, a.qmax, a.e4m3, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
+      quantize_block<D, false>(x, a.gran, a.qmax, a.held, gmax, a.out.k_codes + (static_cast<int64_t>(bh) * a.n_pad + row0) * D,
                                a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
     }
   }
@@ -739,7 +778,7 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.out = out;
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk;
   a.gran = p.gran; a.qmax = p.qmax; a.smooth_q = p.smooth_q; a.smooth_k = p.smooth_k;
-  a.e4m3 = p.qk_e4m3;
+  a.held = p.qk_held;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
   if (p.qk_mx) {

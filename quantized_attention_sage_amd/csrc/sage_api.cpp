@@ -43,14 +43,16 @@ sage_status check_params(const sage_params* p) {
   if (!(p->v_range > 0.f && p->v_range <= 448.f)) return fail(SAGE_EINVAL, "v_range must be in (0, 448]");
   if (!(p->sm_scale >= 0.f) || !std::isfinite(p->sm_scale)) return fail(SAGE_EINVAL, "sm_scale must be finite and >= 0");
   if (p->pv_mode != SAGE_PV_FP8 && p->pv_mode != SAGE_PV_F16) return fail(SAGE_EINVAL, "unknown pv_mode %d", p->pv_mode);
-  if (p->qk_format != SAGE_QK_INT && p->qk_format != SAGE_QK_MXFP4 && p->qk_format != SAGE_QK_INT_E4M3)
+  if (p->qk_format != SAGE_QK_INT && p->qk_format != SAGE_QK_MXFP4 && p->qk_format != SAGE_QK_INT_E4M3 &&
+      p->qk_format != SAGE_QK_INT_E2M3)
     return fail(SAGE_EINVAL, "unknown qk_format %d", p->qk_format);
   if (p->qk_format == SAGE_QK_MXFP4 && p->pv_mode != SAGE_PV_FP8)
     return fail(SAGE_EUNSUPPORTED, "SAGE_QK_MXFP4 is built with SAGE_PV_FP8 only");
-  if (p->qk_format == SAGE_QK_INT_E4M3 && p->qk_bits != 4)
-    return fail(SAGE_EINVAL, "SAGE_QK_INT_E4M3 holds INT4-range codes: qk_bits must be 4 (got %d)", p->qk_bits);
-  if (p->qk_format == SAGE_QK_INT_E4M3 && p->pv_mode != SAGE_PV_FP8)
-    return fail(SAGE_EUNSUPPORTED, "SAGE_QK_INT_E4M3 is built with SAGE_PV_FP8 only");
+  const bool held = p->qk_format == SAGE_QK_INT_E4M3 || p->qk_format == SAGE_QK_INT_E2M3;
+  if (held && p->qk_bits != 4)
+    return fail(SAGE_EINVAL, "SAGE_QK_INT_E4M3 / _E2M3 hold INT4-range codes: qk_bits must be 4 (got %d)", p->qk_bits);
+  if (held && p->pv_mode != SAGE_PV_FP8)
+    return fail(SAGE_EUNSUPPORTED, "SAGE_QK_INT_E4M3 / _E2M3 are built with SAGE_PV_FP8 only");
   return SAGE_OK;
 }
 
@@ -87,7 +89,7 @@ sage::Problem make_problem(const sage_shape* s, const sage_params* p) {
   pr.sm_scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / std::sqrt(static_cast<float>(s->d));
   pr.pv_f16 = p->pv_mode == SAGE_PV_F16;
   pr.qk_mx = p->qk_format == SAGE_QK_MXFP4;
-  pr.qk_e4m3 = p->qk_format == SAGE_QK_INT_E4M3;
+  pr.qk_held = p->qk_format == SAGE_QK_INT_E4M3 ? 1 : (p->qk_format == SAGE_QK_INT_E2M3 ? 2 : 0);
   return pr;
 }
 
@@ -289,8 +291,8 @@ SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void
       (st = check_tensor(v, "v")) || (st = check_qk_buffers(qk)) || (st = check_v_buffers(vb)))
     return st;
   if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
-  if (p->qk_format != SAGE_QK_INT && p->qk_format != SAGE_QK_INT_E4M3)
-    return fail(SAGE_EUNSUPPORTED, "the probe compares integer codes: qk_format must be SAGE_QK_INT or SAGE_QK_INT_E4M3");
+  if (p->qk_format == SAGE_QK_MXFP4)
+    return fail(SAGE_EUNSUPPORTED, "the probe compares integer codes: qk_format must not be SAGE_QK_MXFP4");
   if (p->pv_mode != SAGE_PV_FP8) return fail(SAGE_EUNSUPPORTED, "the probe runs with SAGE_PV_FP8");
   const int64_t nblk = (s->N + 127) / 128;
   if (q_block < 0 || q_block >= nblk)

@@ -25,7 +25,8 @@ struct Problem {
   float p_range, v_range, sm_scale;
   int pv_f16;                    // 1: P~ and V in the 16-bit input type (SAGE_PV_F16)
   int qk_mx;                     // 1: MXFP4 Q and K codes (SAGE_QK_MXFP4)
-  int qk_e4m3;                   // 1: INT4-range integer codes held as E4M3 bytes (SAGE_QK_INT_E4M3)
+  int qk_held;                   // INT4-range codes held as 1: E4M3 bytes (SAGE_QK_INT_E4M3), 2: packed
+                                 // FP6 E2M3 (SAGE_QK_INT_E2M3); 0: int8
 };
 
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,

@@ -80,14 +80,15 @@ def test_layout_sizes(gran, gq, gk):
     assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
 
 
-@pytest.mark.parametrize("mode", ["mxfp4", "pv16", "int_e4m3"])
+@pytest.mark.parametrize("mode", ["mxfp4", "pv16", "int_e4m3", "int_e2m3"])
 def test_layout_sizes_other_formats(mode):
     """MXFP4 codes are 4 bits (d/2 bytes per token) with one scale byte per 32
     channels; the 16-bit P~V keeps V itself (2 bytes per element); E4M3-held
     INT4-range codes take the INT layout byte for byte."""
     B, H, N, d = 2, 3, 1000, 128
     n_pad, BH = 1024, 6
-    kw = {"mxfp4": dict(qk_format=1), "pv16": dict(pv_mode=1), "int_e4m3": dict(qk_format=2, qk_bits=4)}[mode]
+    kw = {"mxfp4": dict(qk_format=1), "pv16": dict(pv_mode=1), "int_e4m3": dict(qk_format=2, qk_bits=4),
+          "int_e2m3": dict(qk_format=3, qk_bits=4)}[mode]
     lay = L.Layout()
     assert L.lib().sage_workspace_layout(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(_params(**kw)),
                                          ctypes.byref(lay)) == L.SAGE_OK
@@ -95,7 +96,7 @@ def test_layout_sizes_other_formats(mode):
         assert lay.q_codes.bytes == lay.k_codes.bytes == BH * n_pad * d // 2
         assert lay.q_scale.bytes == lay.k_scale.bytes == BH * n_pad * d // 32
         assert lay.v_codes.bytes == BH * d * n_pad
-    elif mode == "int_e4m3":
+    elif mode in ("int_e4m3", "int_e2m3"):
         ref = L.Layout()
         L.lib().sage_workspace_layout(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(_params(qk_bits=4)),
                                       ctypes.byref(ref))
@@ -138,7 +139,8 @@ def test_bad_shapes_are_rejected(bad):
 BAD_PARAMS = [dict(qk_bits=6), dict(gran=3), dict(smooth_q=2), dict(p_range=0.0), dict(p_range=449.0),
               dict(v_range=-1.0), dict(sm_scale=-0.5), dict(sm_scale=float("inf")), dict(pv_mode=2),
               dict(qk_format=5), dict(qk_format=1, pv_mode=1),
-              dict(qk_format=2), dict(qk_format=2, qk_bits=4, pv_mode=1)]   # E4M3-held codes: INT4-range, FP8 P~V
+              dict(qk_format=2), dict(qk_format=2, qk_bits=4, pv_mode=1),   # E4M3-held codes: INT4-range, FP8 P~V
+              dict(qk_format=3), dict(qk_format=3, qk_bits=4, pv_mode=1), dict(qk_format=4)]
 
 
 @pytest.mark.parametrize("bad", BAD_PARAMS)

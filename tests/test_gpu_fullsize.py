@@ -25,7 +25,8 @@ FULL = ["llm_prefill", "image_dit", "video_dit", "long_context", "long_context_i
 # the other Q/K and P~V formats at the target shape, and the E4M3-held INT4-range
 # codes on the INT4-range recipes: (recipe, qk_format, pv)
 MODES = [("target", "mxfp4", "fp8"), ("target_causal", "mxfp4", "fp8"), ("target", "int", "f16"),
-         ("long_context_int4", "int_e4m3", "fp8"), ("image_dit", "int_e4m3", "fp8")]
+         ("long_context_int4", "int_e4m3", "fp8"), ("image_dit", "int_e4m3", "fp8"),
+         ("long_context_int4", "int_e2m3", "fp8"), ("image_dit", "int_e2m3", "fp8")]
 
 
 def _heads(w):

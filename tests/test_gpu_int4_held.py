@@ -1,12 +1,13 @@
-"""GPU parity of INT4-range codes held as E4M3 bytes (SAGE_QK_INT_E4M3).
+"""GPU parity of INT4-range codes held in float formats: E4M3 bytes
+(SAGE_QK_INT_E4M3) and packed FP6 E2M3 (SAGE_QK_INT_E2M3).
 
-Every integer in [-7, 7] is exact in E4M3, so the FP8 matrix cores form the
-same integer S = q^ . k^ (fp32 partial sums of integers below 2^24 are
-exact) as the INT8 matrix cores do for the int8-held codes.  The bars:
-codes bit-exact against the oracle's E4M3 bytes, scales and means bit-exact,
-and the output bit-identical to the int8-held INT4-range path on the same
-inputs (which test_gpu_parity.py holds to the oracle's emulation); the
-emulation bar is checked here too.
+Every integer in [-7, 7] is exact in E4M3 and in E2M3, so the FP8 and FP6
+matrix cores form the same integer S = q^ . k^ (fp32 partial sums of
+integers below 2^24 are exact) as the INT8 matrix cores do for the int8-held
+codes.  The bars: codes bit-exact against the oracle's bytes, scales and
+means bit-exact, and the output bit-identical to the int8-held INT4-range
+path on the same inputs (which test_gpu_parity.py holds to the oracle's
+emulation); the emulation bar is checked here too.
 """
 import numpy as np
 import pytest
@@ -14,6 +15,7 @@ import pytest
 import oracle
 from oracle.quant import QuantParams
 from quantized_attention_sage_amd.workloads import WORKLOADS, scaled, make_inputs
+from oracle.fp6 import e2m3_decode, unpack_slots
 from gpu_harness import run_sage, bits, check_output, log, unpermute_v
 
 pytestmark = pytest.mark.gpu
@@ -30,15 +32,21 @@ CASES = {
 }
 
 
+def _decode(codes, fmt):
+    c = np.ascontiguousarray(codes).view(np.uint8)
+    return oracle.e4m3_decode(c) if fmt == "int_e4m3" else e2m3_decode(unpack_slots(c))
+
+
+@pytest.mark.parametrize("fmt", ["int_e4m3", "int_e2m3"])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_int4_e4m3_parity(case):
+def test_int4_held_parity(case, fmt):
     name, kw, gran = CASES[case]
     w = scaled(WORKLOADS[name], **kw)
     q, k, v = make_inputs(w)
-    log(f"int4 e4m3 case {case}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal} gran={gran}")
-    gpu = run_sage(q, k, v, w.dtype, w.causal, qk_bits=4, gran=gran, qk_format="int_e4m3")
+    log(f"int4 {fmt} case {case}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal} gran={gran}")
+    gpu = run_sage(q, k, v, w.dtype, w.causal, qk_bits=4, gran=gran, qk_format=fmt)
     ref = run_sage(q, k, v, w.dtype, w.causal, qk_bits=4, gran=gran, qk_format="int")
-    p = QuantParams(qk_bits=4, gran=gran, qk_format="int_e4m3")
+    p = QuantParams(qk_bits=4, gran=gran, qk_format=fmt)
     qk, vq = oracle.quant_qk(q, k, p), oracle.quant_v(v, p)
     for n in ("q_codes", "k_codes"):
         np.testing.assert_array_equal(gpu[n].view(np.uint8), qk[n], err_msg=n)
@@ -46,7 +54,7 @@ def test_int4_e4m3_parity(case):
         np.testing.assert_array_equal(bits(gpu[n]), bits(qk[n]), err_msg=n)
     np.testing.assert_array_equal(unpermute_v(gpu["v_codes"]), vq["v_codes"], err_msg="v codes")
     # the same numbers as the int8-held codes, and the same output bits
-    np.testing.assert_array_equal(oracle.e4m3_decode(gpu["k_codes"].view(np.uint8)), ref["k_codes"].astype(np.float64))
+    np.testing.assert_array_equal(_decode(gpu["k_codes"], fmt), ref["k_codes"].astype(np.float64))
     np.testing.assert_array_equal(np.asarray(gpu["out"]), np.asarray(ref["out"]), err_msg="output differs from the int8-held path")
     emul = oracle.emulate_attention(qk, vq, w.causal)
     nbad, maxerr, tol = check_output(gpu["out"], emul, v, w.dtype)

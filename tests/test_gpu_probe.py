@@ -30,6 +30,7 @@ CASES = {
     "llm_causal_ragged_last": ("llm_prefill", dict(B=2, H=2, N=300), True, 2, 0.99, "int"),
     "tiny_fp16_d64_first": ("tiny", {}, False, 0, 0.9, "int"),
     "long_causal_first": ("long_context", dict(H=2, N=1100), True, 0, 0.999, "int_e4m3"),
+    "image_dit_e2m3_last": ("image_dit", dict(B=2, H=2, N=333), False, 2, 0.9999, "int_e2m3"),
 }
 
 
