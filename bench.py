@@ -123,7 +123,7 @@ def probe_bench(args, w, qt, kt, vt, shape, ws, dev):
     4 * B * H * rows * keys * d flops (QK dot products and the P V sums)."""
     import torch
     from quantized_attention_sage_amd import api
-    params = api.make_params(qk_bits=4, gran=w.gran, qk_format="int_e4m3" if w.qk_bits == 4 else "int")
+    params = api.make_params(qk_bits=4, gran=w.gran, qk_format="int_e2m3")
     scratch = api.ProbeScratch(shape, dev)
     qb = (w.N - 1) // 128 // 2
     for _ in range(args.warmup):
