@@ -76,6 +76,9 @@ WORKLOADS = {
                        description="B=1 H=32 N=16384 d=128 non-causal attention, INT8 QK, FP8 PV"),
     "target_causal": Workload("target_causal", 1, 32, 16384, 128, "bf16", True, 8, "thread", 6, 3.0,
                               description="B=1 H=32 N=16384 d=128 causal attention, INT8 QK, FP8 PV"),
+    "target_int4": Workload("target_int4", 1, 32, 16384, 128, "bf16", False, 4, "thread", 6, 3.0,
+                            description="B=1 H=32 N=16384 d=128 non-causal attention with SageAttention2's "
+                                        "INT4-range QK, FP8 PV"),
 }
 
 

@@ -14,7 +14,7 @@ from gpu_harness import to_device, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("qk_format,pv", [("int", "fp8"), ("mxfp4", "fp8"), ("int", "f16")])
+@pytest.mark.parametrize("qk_format,pv", [("int", "fp8"), ("mxfp4", "fp8"), ("int", "f16"), ("int_e2m3", "fp8")])
 def test_graph_replay_matches_eager(qk_format, pv):
     import torch
     from quantized_attention_sage_amd import api
@@ -23,7 +23,8 @@ def test_graph_replay_matches_eager(qk_format, pv):
     log(f"graph case qk={qk_format} pv={pv}: H={w.H} N={w.N} causal={w.causal}")
     q, k, v = make_inputs(w)
     qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
-    params = api.make_params(qk_bits=w.qk_bits, gran=w.gran, qk_format=qk_format, pv=pv)
+    bits = 4 if qk_format.startswith("int_") else w.qk_bits     # the held formats carry INT4-range codes
+    params = api.make_params(qk_bits=bits, gran=w.gran, qk_format=qk_format, pv=pv)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, qt.device)
     out = torch.empty_like(qt)
