@@ -87,17 +87,19 @@ __device__ __forceinline__ void map_block(int id, int total, int nblk, int causa
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(void* p) { return (lds_void*)(p); }
 
-// LDS rings of two slots; tile u lives in slot u % 2.  K slot: 128 keys x D
-// codes (rows swizzled).  V slot: D channels x 128 keys of 2 bytes (256-byte
-// rows, swizzled).  Aux slot: the tile's 128 bias values, then its K scales
-// (8 or 2 used).
+// LDS: K and aux rings of two slots (tile u in slot u % 2) and one V slot.
+// K slot: 128 keys x D codes (rows swizzled).  V slot: D channels x 128 keys
+// of 2 bytes (256-byte rows, swizzled); V(t) is copied in during phase B of
+// tile t, after every wave has read V(t-1), and read in phase A of tile t+1.
+// Aux slot: the tile's 128 bias values, then its K scales (8 or 2 used).
+// 66 KiB at d = 128: two work-groups per CU.
 template <int D>
 struct Rings {
   static constexpr int K = kTile * D;
   static constexpr int V = D * kTile * 2;
   static constexpr int AUX = 1024;   // bias (512 B), K scales, spare row at 768
-  static constexpr int K0 = 0, V0 = 2 * K, A0 = 2 * K + 2 * V;
-  static constexpr int BYTES = 2 * (K + V + AUX);
+  static constexpr int K0 = 0, V0 = 2 * K, A0 = 2 * K + V;
+  static constexpr int BYTES = 2 * (K + AUX) + V;
   static constexpr int J = D / 32;   // 1 KiB copies per wave for one K slot
   static constexpr int JV = D / 16;  // ... and for one V slot
 };
@@ -181,11 +183,17 @@ __device__ __forceinline__ void copy_v(uint32_t slot, const TileSrc& s, int k0, 
 // Bias row (waves 0, 1), K scales (wave 2, lanes below s_per_tile) of the 128
 // keys from k0 into an aux slot; wave 3 copies the bias again into a spare row
 // so that every wave issues exactly one copy.
+// The lane's byte offset 4 (64 w + lane) is recomputed at every call (two
+// instructions the compiler may not hoist): held across the loop it is
+// spilled, and the reload's wait would also wait for the tile copies in flight.
 __device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, int k0, int w) {
+  uint32_t lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const uint32_t b_off = 4u * (64u * static_cast<uint32_t>(w) + lane);
   if (w != 2) {
-    dma4(s.b, w == 3 ? (s.b_off & 255u) : s.b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
+    dma4(s.b, w == 3 ? (b_off & 255u) : b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
   } else {
-    const uint32_t lane4 = s.b_off - 512u;
+    const uint32_t lane4 = b_off - 512u;
     dma4(s.s, lane4 < 4u * s.s_per_tile ? lane4 : 0u, static_cast<uint32_t>(4 * (k0 / kTile) * s.s_per_tile),
          slot + 512);
   }
@@ -212,7 +220,7 @@ __device__ __forceinline__ f32x16 mfma_pv16(i32x4 v, i32x4 p, f32x16 acc) {
 // 16-bit P~V: the V slots are twice the FP8 ones (98 KiB of LDS at d = 128),
 // so one work-group runs per CU and the whole register file is available.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_pvh_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // 32-channel k-steps of the QK product
   constexpr int CT = D / 32;          // 32-channel tiles of the output
   constexpr int NQK = 4 * KS;         // QK MFMAs per tile
@@ -267,16 +275,15 @@ __global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
 
   const TileSrc src = make_tile_src<D>(kbase, vbase, brow, kscale, n_kscale, a.n_pad, t);
   // Tile t reads K of tile t+1 (and t's own K only in the prologue), V of tile
-  // t-1 and the aux row of tile t.  It copies K of tile t+2 and the aux row of
-  // tile t+1 when it starts, and V of tile t+1 once every wave has read V of
-  // tile t-1 (mid-tile).  Tile 0's PV product reads the V slot of tile -1,
+  // t-1 and the aux row of tile t.  It copies the aux row of tile t+1 when it
+  // starts, and V of tile t, then K of tile t+2, once every wave has read V of
+  // tile t-1 (mid-tile).  Tile 0's PV product reads the V slot as tile -1,
   // zero-filled here (its P~ is 0 too).
   copy_k<D>(lds0 + R::K0, src, kofs(0), w);
   copy_aux(lds0 + R::A0, src, kofs(0), w);
   copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
-  copy_v<D>(lds0 + R::V0, src, kofs(0), w);
   {
-    uint4* vz = reinterpret_cast<uint4*>(lds + R::V0 + R::V);
+    uint4* vz = reinterpret_cast<uint4*>(lds + R::V0);
 #pragma unroll
     for (int i = t; i < R::V / 16; i += 256) vz[i] = make_uint4(0u, 0u, 0u, 0u);
   }
@@ -332,13 +339,14 @@ __global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
                   __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_slot)::value, NXT = 1 - CUR;
     const int k0 = tt * kTile;
-    // This wave's copy of aux(t) (issued when tile t-1 started) is complete;
-    // only the J + JV copies of K(t+1) and V(t) issued in phase B of tile t-1
-    // may still run (see the mid-tile wait).  After the barrier every wave is
-    // done with aux(t-1), whose slot is refilled below.
-    static_assert(J + JV == 12 || J + JV == 6, "copies per tile");
-    if constexpr (J + JV == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // This wave's copies of aux(t) (issued when tile t-1 started) and of V(t-1)
+    // (issued first in phase B of tile t-1) are complete; only the J copies of
+    // K(t+1) issued after them may still run (see the mid-tile wait).  After
+    // the barrier every wave's V(t-1) is in the slot and every wave is done
+    // with aux(t-1), whose slot is refilled below.
+    static_assert(J == 4 || J == 2, "K copies per tile");
+    if constexpr (J == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     copy_aux(lds0 + R::A0 + NXT * R::AUX, src, kofs(tt + 1), w);
 
     // Fresh copies of the lane offsets: without this the compiler hoists one
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
     // of tile t-1 (V(t-1) is in slot NXT).  LDS operands are fetched ahead of
     // use (bias one quad, V fragments one PV interval) so that a quad's vector
     // work covers their latency.
-    const int vslot_off = R::V0 + NXT * R::V;
+    const int vslot_off = R::V0;
     float x[4][16];
     float mx = -INFINITY, mx2 = -INFINITY;
     i32x4 vh[2 * PPQ];
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
     i32x4 kf[3];
     kf[0] = k_frag(ko, kslot_off, 0, 0);
     if (NQK > 1) kf[1] = k_frag(ko, kslot_off, (1 / KS), 1 % KS);
-    // Every wave has read V(t-1) (its slot is refilled in phase B) and this
+    // Every wave has read V(t-1) (the slot is refilled in phase B) and this
     // wave's copies of K(t+1) are complete (only the aux copy issued at the
     // start of this tile may still run); after the barrier every wave's are.
     asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -453,16 +461,16 @@ __global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
       const int st = i >> 2, q4 = i & 3;
       const int e = i / QK_EVERY;
       if (i % QK_EVERY == 0 && e + 2 < NQK) kf[(e + 2) % 3] = k_frag(ko, kslot_off, (e + 2) / KS, (e + 2) % KS);
-      // Copies for later tiles, one every 16/(2J) quads: K(t+2) into slot CUR
-      // (K(t) was last read in tile t-1) and V(t+1) into slot NXT (freed at
-      // the mid-tile barrier).
+      // Copies, spread evenly over the 16 quads: first V(t) into the V slot
+      // (freed at the mid-tile barrier; read in phase A of tile t+1), then
+      // K(t+2) into K slot CUR (K(t) was last read in tile t-1).
       {
-        constexpr int C = J + JV;   // copies per tile, spread evenly over the 16 quads
+        constexpr int C = J + JV;   // copies per tile
 #pragma unroll
         for (int cj = (i * C + 15) / 16; cj < ((i + 1) * C + 15) / 16; ++cj) {
-          if (cj < J) dma16(src.k, src.k_off, static_cast<uint32_t>(kofs(tt + 2) * D + 4096 * cj),
-                            lds0 + R::K0 + CUR * R::K + (4 * cj + w) * 1024);
-          else copy_v_part(lds0 + R::V0 + NXT * R::V, src, kofs(tt + 1), w, cj - J);
+          if (cj < JV) copy_v_part(lds0 + R::V0, src, kofs(tt), w, cj);
+          else dma16(src.k, src.k_off, static_cast<uint32_t>(kofs(tt + 2) * D + 4096 * (cj - JV)),
+                     lds0 + R::K0 + CUR * R::K + (4 * (cj - JV) + w) * 1024);
         }
       }
       const float p0 = __builtin_amdgcn_exp2f(x[st][4 * q4 + 0] - base);
@@ -497,10 +505,10 @@ __global__ __launch_bounds__(256, 1) void attn_pvh_kernel(AttnArgs a) {
     for (int kc = 0; kc < NPB; ++kc) pA[kc] = pB[kc];
   }
 
-  // PV product of the last tile (V(ntiles-1) was copied mid tile ntiles-2).
+  // PV product of the last tile (V(ntiles-1) was copied in its phase B).
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   {
-    const int lv = R::V0 + ((ntiles - 1) & 1) * R::V;
+    const int lv = R::V0;
 #pragma unroll
     for (int sm = 0; sm < 8; ++sm)
 #pragma unroll
