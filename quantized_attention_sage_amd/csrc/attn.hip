@@ -193,12 +193,19 @@ __device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, int k0
 
 // The same copy with the K scales spread so that subtile st, lane half h
 // reads entry 2 st + h for every granularity (64-key groups: entry j holds
-// group j / 4).  s_src is wave 2's per-lane source offset.
-__device__ __forceinline__ void copy_aux_spread(uint32_t slot, const TileSrc& s, uint32_t s_src, int k0, int w) {
+// group j / 4).  The lane's offsets are recomputed at every call (two
+// instructions the compiler may not hoist): held across the loop they are
+// spilled, and a reload's wait would also wait for the tile copies in flight.
+__device__ __forceinline__ void copy_aux_spread(uint32_t slot, const TileSrc& s, bool thread_gran, int k0, int w) {
+  uint32_t lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   if (w != 2) {
-    dma4(s.b, w == 3 ? (s.b_off & 255u) : s.b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
+    const uint32_t b_off = 4u * (64u * static_cast<uint32_t>(w) + lane);
+    dma4(s.b, w == 3 ? (b_off & 255u) : b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
   } else {
-    dma4(s.s, s_src, static_cast<uint32_t>(4 * (k0 / kTile)) * s.s_per_tile, slot + 512);
+    const uint32_t lane4 = 4u * lane;
+    const uint32_t src = lane4 >= 32u ? 0u : (thread_gran ? lane4 : (lane4 >> 4) << 2);
+    dma4(s.s, src, static_cast<uint32_t>(4 * (k0 / kTile)) * s.s_per_tile, slot + 512);
   }
 }
 
@@ -298,10 +305,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // tile t-1 (mid-tile).  Tile 0's PV product reads the V slot of tile -1,
   // zero-filled here (its P~ is 0 too).
   copy_k<D>(lds0 + R::K0, src, kofs(0), w);
-  // wave 2's K-scale source offsets for copy_aux_spread
-  const uint32_t lane4 = 4u * static_cast<uint32_t>(l);
-  const uint32_t ks_src = lane4 >= 32u ? 0u : (thread_gran ? lane4 : (lane4 >> 4) << 2);
-  if constexpr (F8QK) copy_aux_spread(lds0 + R::A0, src, ks_src, kofs(0), w);
+  if constexpr (F8QK) copy_aux_spread(lds0 + R::A0, src, thread_gran, kofs(0), w);
   else copy_aux(lds0 + R::A0, src, kofs(0), w);
   copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
   copy_v<D>(lds0 + R::V0, src, kofs(0), w);
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // every wave is done with aux(t-1), whose slot is refilled below.
     if constexpr (J == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (F8QK) copy_aux_spread(lds0 + R::A0 + NXT * R::AUX, src, ks_src, kofs(tt + 1), w);
+    if constexpr (F8QK) copy_aux_spread(lds0 + R::A0 + NXT * R::AUX, src, thread_gran, kofs(tt + 1), w);
     else copy_aux(lds0 + R::A0 + NXT * R::AUX, src, kofs(tt + 1), w);
 
     // Fresh copies of the lane offsets: without this the compiler hoists one
