@@ -41,6 +41,7 @@ struct AttnArgs {
   int H, N, n_pad, nblk, gran, causal;
   float scale_log2;  // sm_scale * log2(e)
   float log2_pr;     // log2(P_r)
+  int lpt_g;         // causal: heads per longest-first group (map_block)
 };
 
 // 16-byte chunk swizzle inside a tile row so that the 16 lanes served together
@@ -63,13 +64,24 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float x) {
 // give every XCD a contiguous run of (head, block) items: the K/V codes of one
 // head then stay in that XCD's L2 while its blocks run.  Causal runs visit the
 // blocks of a head from the last (longest) to the first.
-__device__ __forceinline__ void map_block(int id, int total, int nblk, int causal, int& bh, int& qb) {
+__device__ __forceinline__ void map_block(int id, int total, int nblk, int causal, int lpt_g, int& bh, int& qb) {
   constexpr int kXcd = 8;
   int w = id;
   if (total % kXcd == 0) w = (id % kXcd) * (total / kXcd) + id / kXcd;
   bh = w / nblk;
   qb = w % nblk;
-  if (causal) qb = nblk - 1 - qb;
+  if (causal) {
+    qb = nblk - 1 - qb;
+    // Groups of lpt_g heads that stay within one XCD run block-major, so the
+    // longest blocks of the group go first (the K/V codes of lpt_g heads fit
+    // that XCD's L2; the host picks lpt_g).
+    const int span = lpt_g * nblk, g0 = (w / span) * span;
+    if (lpt_g > 1 && total % kXcd == 0 && (total / kXcd) % span == 0) {
+      const int loc = w - g0;
+      bh = g0 / nblk + loc % lpt_g;
+      qb = nblk - 1 - loc / lpt_g;
+    }
+  }
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
   const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, held in a scalar register
   int bh, qb;
-  map_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), a.nblk, a.causal, bh, qb);
+  map_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x), a.nblk, a.causal, a.lpt_g, bh, qb);
   const int q0 = qb * 128;
   const int qi = q0 + 32 * w + col;
 
@@ -540,6 +552,7 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.gran = p.gran; a.causal = causal ? 1 : 0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.log2_pr = log2f(p.p_range);
+  a.lpt_g = lpt_group(p.B * p.H, static_cast<int64_t>(p.n_pad) * (p.D + p.D / 2 + p.D / 32));
   hipLaunchKernelGGL((attn_fp4_kernel<D, BF16>), dim3(p.nblk * p.B * p.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -42,6 +42,17 @@ hipError_t launch_attn_fp4(const Problem& p, const sage_qk_buffers& qk, const sa
 hipError_t launch_attn_pvh(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
 
+// Heads per longest-first group of a causal grid: as many heads (a power of
+// two dividing the heads of one XCD, at most 8) as keep their streamed K/V
+// bytes within 4 MiB, one XCD's L2.
+inline int lpt_group(int heads, int64_t head_bytes) {
+  if (heads % 8 != 0) return 1;
+  const int per_xcd = heads / 8;
+  int g = 1;
+  while (g < 8 && per_xcd % (2 * g) == 0 && 2 * g * head_bytes <= (int64_t(4) << 20)) g *= 2;
+  return g;
+}
+
 // Scratch of the adaptive INT4/INT8 probe (byte offsets, 256-byte aligned).
 struct ProbeLayout {
   size_t ref, o4, o8, part, sums, total, bytes;
