@@ -287,13 +287,20 @@ SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void
                                         const sage_qk_buffers* qk, const sage_v_buffers* vb, void* scratch,
                                         size_t scratch_bytes, sage_probe_result* result, void* stream) {
   sage_status st;
-  if ((st = check_shape(s)) || (st = check_params(p)) || (st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) ||
-      (st = check_tensor(v, "v")) || (st = check_qk_buffers(qk)) || (st = check_v_buffers(vb)))
-    return st;
-  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  if (!p) return fail(SAGE_EINVAL, "params is NULL");
   if (p->qk_format == SAGE_QK_MXFP4)
     return fail(SAGE_EUNSUPPORTED, "the probe compares integer codes: qk_format must not be SAGE_QK_MXFP4");
   if (p->pv_mode != SAGE_PV_FP8) return fail(SAGE_EUNSUPPORTED, "the probe runs with SAGE_PV_FP8");
+  // p->qk_bits is ignored: the two passes use 8 (SAGE_QK_INT) and 4 (p->qk_format)
+  sage_params p8 = *p, p4 = *p;
+  p8.qk_bits = 8;
+  p8.qk_format = SAGE_QK_INT;
+  p4.qk_bits = 4;
+  if ((st = check_shape(s)) || (st = check_params(&p8)) || (st = check_params(&p4)) || (st = check_tensor(q, "q")) ||
+      (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) || (st = check_qk_buffers(qk)) ||
+      (st = check_v_buffers(vb)))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
   const int64_t nblk = (s->N + 127) / 128;
   if (q_block < 0 || q_block >= nblk)
     return fail(SAGE_EINVAL, "q_block must be in [0, %lld) (got %lld)", (long long)nblk, (long long)q_block);
@@ -304,10 +311,6 @@ SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void
                                                   static_cast<int>(s->N), static_cast<int>(s->d), 2);
   if (scratch_bytes < PL.bytes) return fail(SAGE_EINVAL, "scratch too small: %zu < %zu bytes", scratch_bytes, PL.bytes);
 
-  sage_params p8 = *p, p4 = *p;
-  p8.qk_bits = 8;
-  p8.qk_format = SAGE_QK_INT;
-  p4.qk_bits = 4;
   const sage::Problem pr8 = make_problem(s, &p8), pr4 = make_problem(s, &p4);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const sage::TensorView qv{q, s->q_stride[0], s->q_stride[1], s->q_stride[2]};

@@ -31,6 +31,8 @@ CASES = {
     "tiny_fp16_d64_first": ("tiny", {}, False, 0, 0.9, "int"),
     "long_causal_first": ("long_context", dict(H=2, N=1100), True, 0, 0.999, "int_e4m3"),
     "image_dit_e2m3_last": ("image_dit", dict(B=2, H=2, N=333), False, 2, 0.9999, "int_e2m3"),
+    # the caller's qk_bits is ignored (8 here, with an INT4-range-only format)
+    "target_bits_ignored": ("target", dict(H=2, N=300), False, 1, 0.999, "int_e2m3", 8),
 }
 
 
@@ -38,7 +40,7 @@ CASES = {
 def test_probe(case):
     import torch
     from quantized_attention_sage_amd import api
-    name, kw, causal, qb, cos_min, fmt4 = CASES[case]
+    name, kw, causal, qb, cos_min, fmt4, *given = CASES[case]
     w = scaled(WORKLOADS[name], **kw)
     q, k, v = make_inputs(w)
     log(f"probe case {case}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={causal} block={qb} fmt={fmt4}")
@@ -46,6 +48,8 @@ def test_probe(case):
     params = api.make_params(qk_bits=4, gran=w.gran, qk_format=fmt4)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, qt.device)
+    if given:
+        params.qk_bits = given[0]
     scratch = api.ProbeScratch(shape, qt.device)
     res = api.probe_qk_bits(qt, kt, vt, params, ws, shape, causal, qb, cos_min, scratch)
     torch.cuda.synchronize()
