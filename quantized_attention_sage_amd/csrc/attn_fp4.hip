@@ -268,7 +268,10 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = t; i < R::V / 16; i += 256) vz[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // K(0) and aux(0) are needed now; the J + 1 + JV copies of K(1) and V(0)
+  // may still run (they are what the first tile-start wait allows for).
+  if constexpr (J + 1 + JV == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // Per-lane byte offsets of the LDS fragments, relative to a slot.  The
   // swizzle term does not depend on the subtile (K) or the channel tile (V),
