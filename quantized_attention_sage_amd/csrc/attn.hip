@@ -150,7 +150,7 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, u
 // channel rows of V).
 struct TileSrc {
   i32x4 k, v, b, s;
-  uint32_t k_off, v_off, b_off;   // per-lane byte offsets for j = 0 and k0 = 0
+  uint32_t k_off, v_off;          // per-lane byte offsets for j = 0 and k0 = 0
   uint32_t v_row;                 // bytes per V channel row (n_pad)
   uint32_t s_per_tile;            // K scale groups per 128-key tile (8 or 2)
 };
@@ -169,7 +169,6 @@ __device__ __forceinline__ TileSrc make_tile_src(const int8_t* kbase, const uint
   s.k_off = static_cast<uint32_t>(r * D + 16 * swz<D>(r, pc));
   const int ch = t >> 3, vc = t & 7;
   s.v_off = static_cast<uint32_t>(ch * n_pad + 16 * swz<128>(ch, vc));
-  s.b_off = static_cast<uint32_t>(4 * t);
   s.v_row = static_cast<uint32_t>(n_pad);
   return s;
 }
@@ -190,25 +189,14 @@ __device__ __forceinline__ void copy_v(uint32_t slot, const TileSrc& s, int k0, 
     dma16(s.v, s.v_off, static_cast<uint32_t>(k0) + 32u * j * s.v_row, slot + (4 * j + w) * 1024);
 }
 
-// Bias row (waves 0, 1), K scales (wave 2, lanes below s_per_tile) of the 128
-// keys from k0 into an aux slot; wave 3 copies the bias again into a spare row
-// so that every wave issues exactly one copy.
-__device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, int k0, int w) {
-  if (w != 2) {
-    dma4(s.b, w == 3 ? (s.b_off & 255u) : s.b_off, static_cast<uint32_t>(4 * k0), slot + (w == 3 ? 768 : 256 * w));
-  } else {
-    const uint32_t lane4 = s.b_off - 512u;
-    dma4(s.s, lane4 < 4u * s.s_per_tile ? lane4 : 0u, static_cast<uint32_t>(4 * (k0 / kTile) * s.s_per_tile),
-         slot + 512);
-  }
-}
-
-// The same copy with the K scales spread so that subtile st, lane half h
-// reads entry 2 st + h for every granularity (64-key groups: entry j holds
+// Bias row (waves 0, 1) and K scales (wave 2) of the 128 keys from k0 into an
+// aux slot; wave 3 copies the bias again into a spare row so that every wave
+// issues exactly one copy.  The K scales are spread so that subtile st, lane
+// half h reads entry 2 st + h for every granularity (64-key groups: entry j holds
 // group j / 4).  The lane's offsets are recomputed at every call (two
 // instructions the compiler may not hoist): held across the loop they are
 // spilled, and a reload's wait would also wait for the tile copies in flight.
-__device__ __forceinline__ void copy_aux_spread(uint32_t slot, const TileSrc& s, bool thread_gran, int k0, int w) {
+__device__ __forceinline__ void copy_aux(uint32_t slot, const TileSrc& s, bool thread_gran, int k0, int w) {
   uint32_t lane;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   if (w != 2) {
@@ -317,8 +305,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   // tile t-1 (mid-tile).  Tile 0's PV product reads the V slot of tile -1,
   // zero-filled here (its P~ is 0 too).
   copy_k<D>(lds0 + R::K0, src, kofs(0), w);
-  if constexpr (F8QK) copy_aux_spread(lds0 + R::A0, src, thread_gran, kofs(0), w);
-  else copy_aux(lds0 + R::A0, src, kofs(0), w);
+  copy_aux(lds0 + R::A0, src, thread_gran, kofs(0), w);
   copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
   copy_v<D>(lds0 + R::V0, src, kofs(0), w);
   {
@@ -418,8 +405,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // every wave is done with aux(t-1), whose slot is refilled below.
     if constexpr (J == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (F8QK) copy_aux_spread(lds0 + R::A0 + NXT * R::AUX, src, thread_gran, kofs(tt + 1), w);
-    else copy_aux(lds0 + R::A0 + NXT * R::AUX, src, kofs(tt + 1), w);
+    copy_aux(lds0 + R::A0 + NXT * R::AUX, src, thread_gran, kofs(tt + 1), w);
 
     // Fresh copies of the lane offsets: without this the compiler hoists one
     // address register per (slot, fragment) out of the loop and spills them.
@@ -440,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       const float* ksc = reinterpret_cast<const float*>(lds + aux + 512);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        cs[st] = dq2 * (F8QK ? ksc[2 * st + hh] : (thread_gran ? ksc[2 * st + hh] : ksc[st >> 1]));
+        cs[st] = dq2 * ksc[2 * st + hh];
     }
 
     // Phase A: dequantise S(t) and take the row maximum, beside the PV product
