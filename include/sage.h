@@ -23,8 +23,9 @@
  *
  * All entry points are plain C with device pointers, sizes and a HIP stream
  * (passed as void*, a hipStream_t; NULL is the default stream).  The library
- * never allocates or frees memory: the caller owns every buffer.  Nothing
- * synchronises; every call only enqueues work on the given stream.
+ * never allocates or frees memory: the caller owns every buffer.  Apart from
+ * sage_probe_qk_bits, which waits for its sums, nothing synchronises: every
+ * call only enqueues work on the given stream.
  *
  * Error behaviour: every argument is validated on the host before anything is
  * enqueued.  A call that returns an error has launched nothing and written
