@@ -168,8 +168,8 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic figure")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard across GPUs with no communication; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path here "
+              "(heads would shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   SAGE_OK = 0,
   SAGE_EINVAL = 1,       /* bad pointer, shape, stride, alignment or size */
-  SAGE_EUNSUPPORTED = 2, /* valid request outside what this build supports */
+  SAGE_EUNSUPPORTED = 2, /* valid request outside what this library supports */
   SAGE_EHIP = 3          /* the HIP runtime reported an error */
 } sage_status;
 

@@ -5,7 +5,7 @@ scales; P~ and V to FP8; smoothing of Q and V; SageAttention's K smoothing
 among the "precision-enhancing methods") and the SageAttention2++ summary,
 "2.1 SageAttention2" (Q and K use per-block scales, V per-channel scales).
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * K smoothing subtracts the per-channel mean over all N tokens of a head.
   * Q smoothing subtracts the per-channel mean of each 128-token block; the
     lost term comes back as the bias dS[qb, j] = mu_Q(qb) . K'_j (unquantised K').

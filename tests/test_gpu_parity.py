@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Bars (written here, derived in the design doc):
+Bars (derived from the arithmetic of each step):
   * codes, scales and means: bit-exact against the oracle's fp32 emulation;
   * bias dS: |err| <= 2^-14 sum_c |mu_Q,c| |K'_jc| (bf16 hi/lo split products);
   * output: |O_gpu - O_emul| <= 2e-3 max|V| + half an fp16/bf16 ulp of O;

@@ -3,7 +3,7 @@ MXFP4 score path.
 
 E2M1 and E8M0 follow the OCP microscaling format definition (1 sign, 2
 exponent bits with bias 1, 1 mantissa bit; scale byte e = 2^(e - 127)); the
-block exponent rule (smallest s with 6 * 2^s >= amax) is this build's reading
+block exponent rule (smallest s with 6 * 2^s >= amax) is a reading
 of the SageAttention3 abstract's FP4 microscaling, stated in oracle/fp4.py.
 """
 import math
