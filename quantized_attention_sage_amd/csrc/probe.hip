@@ -9,12 +9,13 @@
 // distance against full-precision attention.
 //
 //  * exact_part_kernel: work-group (split s, head bh) runs a plain fp32 online
-//    softmax over the keys of split s for the 128 rows of the block.  Eight
-//    lanes share four rows, each holding an eighth of q and of the four output
-//    rows, so that every K or V value read from LDS feeds four FMAs (LDS
-//    bandwidth, not the FMA rate, bounds this loop otherwise); a score is the
-//    sum of the eight partial dot products.  K and V sub-tiles of 8 keys are
-//    staged in LDS as fp32.
+//    softmax over the keys of split s for the 128 rows of the block, on the
+//    fp32 matrix cores (v_mfma_f32_32x32x2_f32, fp32 products and sums).  As
+//    in the quantized kernel, S^T = K Q^T puts one query and 16 keys in each
+//    lane, so the row maximum takes one exchange with lane l ^ 32 and the
+//    lane's P values are directly the B operand of O^T += V^T P^T.  K and V
+//    sub-tiles of 64 keys are staged in LDS as fp32 (V transposed), the next
+//    one's loads in flight during the current one's products.
 //  * exact_merge_kernel: one work-group per (head, row), one lane per channel,
 //    combines the splits (max of the running maxima, then the weighted sums)
 //    into the reference rows.
@@ -26,7 +27,7 @@ namespace sage {
 namespace {
 
 constexpr int kRows = 128;   // one query block
-constexpr int kSub = 8;      // keys per LDS sub-tile
+constexpr int kSub = 8;      // split lengths past 64 Ki keys are multiples of this
 
 template <bool BF16>
 __device__ __forceinline__ float ld16(const void* base, int64_t i) {
@@ -61,139 +62,146 @@ __device__ __forceinline__ void cvt8(uint4 u, float (&f)[8]) {
   }
 }
 
-// Sum over each aligned group of 8 lanes, with DPP lane moves (no LDS
-// round trip): swap neighbours, swap pairs, then mirror within the 8.
-__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
-  const int v = __float_as_int(x);
-  int r;
-  if (ctrl_sel == 0) r = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
-  else if (ctrl_sel == 1) r = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  else r = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);                     // row_half_mirror
-  return __int_as_float(r);
-}
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp_f(x, 0);
-  x += dpp_f(x, 1);
-  return x + dpp_f(x, 2);
-}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void exact_part_kernel(ExactArgs a) {
-  constexpr int LPR = 8;          // lanes sharing a row
-  constexpr int RPL = 4;          // rows per lane: each value read from LDS feeds RPL FMAs
-  constexpr int DQ = D / LPR;     // channels per lane
-  constexpr int RS = DQ + 4;      // segment stride in LDS: the eight segments fall in different banks
-  __shared__ __attribute__((aligned(16))) float ks[kSub][LPR][RS];
-  __shared__ __attribute__((aligned(16))) float vs[kSub][LPR][RS];
-  const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  const int g = l / LPR, qd = l % LPR;
-  // rows of this lane: 32 w + g + 8 u, u < RPL; channels DQ qd ..
+__global__ __launch_bounds__(256, 2) void exact_part_kernel(ExactArgs a) {
+  constexpr int KT = 64;                 // keys per LDS sub-tile
+  constexpr int KR = D + 4;              // K row stride (floats): a wave's 32 rows fall in different banks
+  constexpr int VR = KT + 4;             // V^T row stride (floats)
+  constexpr int HC = D / 2;              // channels per lane half
+  constexpr int CT = D / 32;             // 32-channel output tiles
+  constexpr int PF = KT * D / 8 / 256;   // 16-byte loads per thread, tensor and sub-tile
+  __shared__ __attribute__((aligned(16))) float kl[KT * KR];   // K [key][channel]
+  __shared__ __attribute__((aligned(16))) float vt[D * VR];    // V^T [channel][key]
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, col = l & 31, hh = l >> 5;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
+  const int qi = a.q0 + 32 * w + col;    // this lane's query (column of the 32x32 products)
 
-  float q[RPL][DQ], o[RPL][DQ], m[RPL], lsum[RPL];
-  int qi[RPL];
+  // B operand of product i (i < HC): Q[qi][HC hh + i], so that one product
+  // pairs channel i (lanes 0-31) with channel HC + i (lanes 32-63).
+  float qr[HC];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qs0 + h * a.qs1 +
+                           static_cast<int64_t>(min(qi, a.N - 1)) * a.qs2 + HC * hh;
 #pragma unroll
-  for (int u = 0; u < RPL; ++u) {
-    qi[u] = a.q0 + 32 * w + g + 8 * u;
-    const int64_t base = b * a.qs0 + h * a.qs1 + static_cast<int64_t>(min(qi[u], a.N - 1)) * a.qs2 + qd * DQ;
+    for (int c8 = 0; c8 < HC / 8; ++c8) {
+      float f[8];
+      cvt8<BF16>(*reinterpret_cast<const uint4*>(qrow + 8 * c8), f);
 #pragma unroll
-    for (int c = 0; c < DQ; ++c) {
-      q[u][c] = qi[u] < a.N ? ld16<BF16>(a.q, base + c) : 0.f;
-      o[u][c] = 0.f;
+      for (int e = 0; e < 8; ++e) qr[8 * c8 + e] = qi < a.N ? f[e] : 0.f;
     }
-    m[u] = -INFINITY;
-    lsum[u] = 0.f;
   }
+  f32x16 oacc[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
 
   const int kb = split * a.chunk, ke = min(a.key_end, kb + a.chunk);
-  const int64_t kbase = b * a.ks0 + h * a.ks1, vbase = b * a.vs0 + h * a.vs1;
-  constexpr int LOADS = kSub * D / 8;   // 16-byte loads per sub-tile and tensor
-  for (int j0 = kb; j0 < ke; j0 += kSub) {
-    __syncthreads();
-    if (t < LOADS) {
-      const int jj = t / (D / 8), c = 8 * (t % (D / 8)), j = j0 + jj;
-      float fk[8], fv[8];
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1;
+  // Load p of a sub-tile: key (t + 256 p) / (D/8), channels 8 ((t + 256 p) % (D/8)) ..; keys past ke read as 0.
+  uint4 kp[PF], vp[PF];
+  auto fetch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int idx = t + 256 * p, kk = idx / (D / 8), c = 8 * (idx % (D / 8)), j = j0 + kk;
+      kp[p] = vp[p] = make_uint4(0u, 0u, 0u, 0u);
       if (j < ke) {
-        cvt8<BF16>(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + kbase +
-                                                   static_cast<int64_t>(j) * a.ks2 + c), fk);
-        cvt8<BF16>(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + vbase +
-                                                   static_cast<int64_t>(j) * a.vs2 + c), fv);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) fk[i] = fv[i] = 0.f;
+        kp[p] = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(j) * a.ks2 + c);
+        vp[p] = *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(j) * a.vs2 + c);
       }
-      float* kd = &ks[jj][c / DQ][c % DQ];
-      float* vd = &vs[jj][c / DQ][c % DQ];
+    }
+  };
+  if (kb < ke) fetch(kb);
+  for (int j0 = kb; j0 < ke; j0 += KT) {
+    __syncthreads();   // every wave is done with the previous sub-tile
 #pragma unroll
-      for (int i = 0; i < 8; i += 4) {
-        *reinterpret_cast<float4*>(kd + i) = make_float4(fk[i], fk[i + 1], fk[i + 2], fk[i + 3]);
-        *reinterpret_cast<float4*>(vd + i) = make_float4(fv[i], fv[i + 1], fv[i + 2], fv[i + 3]);
-      }
+    for (int p = 0; p < PF; ++p) {
+      const int idx = t + 256 * p, kk = idx / (D / 8), c = 8 * (idx % (D / 8));
+      float fk[8], fv[8];
+      cvt8<BF16>(kp[p], fk);
+      cvt8<BF16>(vp[p], fv);
+      *reinterpret_cast<float4*>(&kl[kk * KR + c]) = make_float4(fk[0], fk[1], fk[2], fk[3]);
+      *reinterpret_cast<float4*>(&kl[kk * KR + c + 4]) = make_float4(fk[4], fk[5], fk[6], fk[7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(c + e) * VR + kk] = fv[e];
     }
     __syncthreads();
-    float sc[RPL][kSub];
-    float mt[RPL];
+    if (j0 + KT < ke) fetch(j0 + KT);   // the next sub-tile's loads fly during this one's products
 #pragma unroll
-    for (int u = 0; u < RPL; ++u) mt[u] = -INFINITY;
+    for (int s = 0; s < KT / 32; ++s) {
+      // S^T of keys j0 + 32 s ..: A operand of product i is K[key 32 s + col][HC hh + i].
+      f32x16 sacc;
 #pragma unroll
-    for (int jj = 0; jj < kSub; ++jj) {
-      float kr[DQ];
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      const float* krow = &kl[(32 * s + col) * KR + HC * hh];
 #pragma unroll
-      for (int c = 0; c < DQ; ++c) kr[c] = ks[jj][qd][c];
-      const int j = j0 + jj;
-      float dot[RPL];
-#pragma unroll
-      for (int u = 0; u < RPL; ++u) dot[u] = 0.f;
-#pragma unroll
-      for (int c = 0; c < DQ; ++c)     // rows innermost: RPL independent FMA chains
-#pragma unroll
-        for (int u = 0; u < RPL; ++u) dot[u] = fmaf(q[u][c], kr[c], dot[u]);
-#pragma unroll
-      for (int u = 0; u < RPL; ++u) {
-        const float d8 = sum8(dot[u]);
-        const bool vis = j < ke && (!a.causal || j <= qi[u]);
-        sc[u][jj] = vis ? d8 * a.scale_log2 : -INFINITY;
-        mt[u] = fmaxf(mt[u], sc[u][jj]);
+      for (int i4 = 0; i4 < HC / 4; ++i4) {
+        const float4 kv = *reinterpret_cast<const float4*>(krow + 4 * i4);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qr[4 * i4 + 0], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qr[4 * i4 + 1], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qr[4 * i4 + 2], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qr[4 * i4 + 3], sacc, 0, 0, 0);
       }
-    }
-    float mn[RPL];
+      // sacc[i]: key j0 + 32 s + 8 (i / 4) + 4 hh + i % 4 of query qi; lane l ^ 32 holds the other 16 keys.
+      float sc[16];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < RPL; ++u) {
-      mn[u] = fmaxf(m[u], mt[u]);
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + 32 * s + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const bool vis = j < ke && (!a.causal || j <= qi);
+        sc[i] = vis ? sacc[i] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, sc[i]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
       // alpha = 0 while m is -inf; a row with no visible key yet keeps m = -inf, o = 0, l = 0
-      const float alpha = mn[u] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[u] - mn[u]);
-      lsum[u] *= alpha;
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      float ps = 0.f;
 #pragma unroll
-      for (int c = 0; c < DQ; ++c) o[u][c] *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - mn);
+        ps += sc[i];
+      }
+      lsum = lsum * alpha + ps;
+      m = mn;
 #pragma unroll
-      for (int jj = 0; jj < kSub; ++jj)
-        sc[u][jj] = mn[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[u][jj] - mn[u]);
-      m[u] = mn[u];
-    }
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int jj = 0; jj < kSub; ++jj) {
-      float vr[DQ];
+        for (int i = 0; i < 16; ++i) oacc[c][i] *= alpha;
+      // O^T += V^T P^T: A operand V[key 32 s + 8 jq + 4 hh + e][32 c + col], B operand this lane's P.
 #pragma unroll
-      for (int c = 0; c < DQ; ++c) vr[c] = vs[jj][qd][c];
+      for (int c = 0; c < CT; ++c) {
+        const float* vrow = &vt[(32 * c + col) * VR + 32 * s + 4 * hh];
 #pragma unroll
-      for (int u = 0; u < RPL; ++u) {
-        lsum[u] += sc[u][jj];
-#pragma unroll
-        for (int c = 0; c < DQ; ++c) o[u][c] = fmaf(sc[u][jj], vr[c], o[u][c]);
+        for (int jq = 0; jq < 4; ++jq) {
+          const float4 vv = *reinterpret_cast<const float4*>(vrow + 8 * jq);
+          oacc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, sc[4 * jq + 0], oacc[c], 0, 0, 0);
+          oacc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, sc[4 * jq + 1], oacc[c], 0, 0, 0);
+          oacc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, sc[4 * jq + 2], oacc[c], 0, 0, 0);
+          oacc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, sc[4 * jq + 3], oacc[c], 0, 0, 0);
+        }
       }
     }
   }
+  // oacc[c][i]: channel 32 c + 8 (i / 4) + 4 hh + i % 4 of query qi
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  float* dst = a.part + ((static_cast<int64_t>(split) * gridDim.y + bh) * kRows + 32 * w + col) * (D + 2);
 #pragma unroll
-  for (int u = 0; u < RPL; ++u) {
-    const int r = 32 * w + g + 8 * u;
-    float* dst = a.part + ((static_cast<int64_t>(split) * gridDim.y + bh) * kRows + r) * (D + 2);
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int c = 0; c < DQ; ++c) dst[qd * DQ + c] = o[u][c];
-    if (qd == 0) {
-      dst[D] = m[u];
-      dst[D + 1] = lsum[u];
+    for (int jq = 0; jq < 4; ++jq) {
+      float* d = dst + 32 * c + 8 * jq + 4 * hh;    // rows are (D + 2) floats: 8-byte aligned
+      *reinterpret_cast<float2*>(d) = make_float2(oacc[c][4 * jq + 0], oacc[c][4 * jq + 1]);
+      *reinterpret_cast<float2*>(d + 2) = make_float2(oacc[c][4 * jq + 2], oacc[c][4 * jq + 3]);
     }
+  if (hh == 0) {
+    dst[D] = m;
+    dst[D + 1] = ltot;
   }
 }
 
@@ -277,7 +285,7 @@ ProbeLayout probe_layout(int B, int H, int N, int D, int io_bytes) {
   ProbeLayout L;
   const int64_t BH = static_cast<int64_t>(B) * H;
   const int n_pad = (N + 127) / 128 * 128;
-  // at most 64 key splits; splits are whole 32-key sub-tiles
+  // at most 64 key splits (a split's last sub-tile may be partly past its end, masked)
   L.chunk = n_pad <= 64 * 1024 ? 1024 : ((n_pad + 63) / 64 + kSub - 1) / kSub * kSub;
   L.splits = (n_pad + L.chunk - 1) / L.chunk;
   size_t off = 0;
