@@ -261,17 +261,18 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
   // zero-filled here (its P~ is 0 too).
   copy_k<D>(lds0 + R::K0, src, kofs(0), w);
   copy_aux(lds0 + R::A0, src, kofs(0), w);
-  copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
-  copy_v<D>(lds0 + R::V0, src, kofs(0), w);
   {
     uint4* vz = reinterpret_cast<uint4*>(lds + R::V0 + R::V);
 #pragma unroll
     for (int i = t; i < R::V / 16; i += 256) vz[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  // K(0) and aux(0) are needed now; the J + 1 + JV copies of K(1) and V(0)
-  // may still run (they are what the first tile-start wait allows for).
-  if constexpr (J + 1 + JV == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // K(0) and aux(0) are needed now.  They are waited for by count 0, which
+  // assumes nothing about the completion order of copies of different sizes;
+  // the copies of K(1) and V(0) are issued after the barrier and run beside the first
+  // QK product (they are what the first tile-start wait allows for).
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  copy_k<D>(lds0 + R::K0 + R::K, src, kofs(1), w);
+  copy_v<D>(lds0 + R::V0, src, kofs(0), w);
 
   // Per-lane byte offsets of the LDS fragments, relative to a slot.  The
   // swizzle term does not depend on the subtile (K) or the channel tile (V),
@@ -404,7 +405,13 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // K fragments of the first two QK MFMAs of phase B.
+    // Every wave has read V(t-1) (its slot is refilled in phase B) and this
+    // wave's copies of K(t+1) are complete (only the aux copy issued at the
+    // start of this tile may still run); after the barrier every wave's are.
+    asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // K fragments of the first two QK MFMAs of phase B, read only now: K(t+1)
+    // is copied by all four waves, and only the barrier above makes every
+    // wave's part of it visible.
     const int kslot_off = R::K0 + NXT * R::K;
     i32x4 kf[3];
     int kfs[3];
@@ -414,10 +421,6 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
       kf[1] = k_frag(ko, kslot_off, (1 / KS), 1 % KS);
       kfs[1] = k_scale(ksl, kslot_off, (1 / KS), 1 % KS);
     }
-    // Every wave has read V(t-1) (its slot is refilled in phase B) and this
-    // wave's copies of K(t+1) are complete (only the aux copy issued at the
-    // start of this tile may still run); after the barrier every wave's are.
-    asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     mx = fmaxf(mx, mx2);
     const bool need_mask = (k0 + kTile > a.N) || (a.causal && k0 + kTile - 1 > q0 + 32 * w);
