@@ -262,24 +262,30 @@ struct QKArgs {
   sage_qk_buffers out;
   int H, N, n_pad, nblk, gran, qmax, smooth_q, smooth_k;
   int held;   // INT4-range integer codes written as 1: E4M3 bytes, 2: packed FP6 E2M3 (0: int8)
+  int with_bias;     // 0: K codes and scales only; the bias buffer is left as it is
+  int k_sums;        // 0: pass 1 skips the K block sums (k_partial and k_mean are left as they are)
+  int q_blk0;        // pass 1's first Q block (its grid spans the Q blocks it quantizes)
   float scale_log2;  // sm_scale * log2(e): the bias is stored in the exp2 domain
 };
 
 // Pass 1, two work-groups per (128-token block, head): blockIdx.z = 0 writes
 // the block's K channel sums (subtrees of the K mean's tree), z = 1 the Q
-// block mean, Q codes and scales.
+// block mean, Q codes and scales.  With k_sums = 0 every work-group is a Q one,
+// for Q blocks q_blk0 + blockIdx.x.
 template <int D, bool BF16, bool MX>
 __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
   __shared__ float lds[4 * D];
   __shared__ unsigned gmax[128];
-  const int blk = blockIdx.x, bh = blockIdx.y;
+  const bool k_part = a.k_sums && blockIdx.z == 0;
+  const int blk = k_part ? static_cast<int>(blockIdx.x) : a.q_blk0 + static_cast<int>(blockIdx.x);
+  const int bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
   const int row0 = blk * 128;
   const int t = threadIdx.x, g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
   float x[Tile<D>::TOK][8];
   float s[8];
 
-  if (blockIdx.z == 0) {
+  if (k_part) {
     // K block sums.
     load_block<D, BF16>(a.k + b * a.ksB + h * a.ksH, a.ksN, row0, a.N, x);
     block_tree_sum<D>(x, s, lds);
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
     }
   };
-  fetch_mu(0);
+  if (a.with_bias) fetch_mu(0);
 
   {
     float x[Tile<D>::TOK][8];
@@ -467,6 +473,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                                a.out.k_scale + (static_cast<int64_t>(bh) * a.nblk + blk) * ngk);
     }
   }
+
+  if (!a.with_bias) return;   // uniform over the launch
 
   // B operand: the split K' of this wave's 32 keys (the block's rows read
   // again, from L2), 16 channels per MFMA step, lane half hh holding 8.
@@ -769,7 +777,8 @@ __global__ __launch_bounds__(kThreads) void v_pack16_kernel(VArgs a) {
 }
 
 template <int D, bool BF16>
-hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out, hipStream_t st) {
+hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out, hipStream_t st,
+                         const QKPart& part) {
   QKArgs a;
   a.q = static_cast<const uint16_t*>(q.ptr);
   a.k = static_cast<const uint16_t*>(k.ptr);
@@ -779,16 +788,22 @@ hipError_t quant_qk_impl(const Problem& p, TensorView q, TensorView k, const sag
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk;
   a.gran = p.gran; a.qmax = p.qmax; a.smooth_q = p.smooth_q; a.smooth_k = p.smooth_k;
   a.held = p.qk_held;
+  a.with_bias = part.bias ? 1 : 0;
+  a.k_sums = part.k_sums ? 1 : 0;
+  a.q_blk0 = part.k_sums ? 0 : part.q_blk0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   const dim3 grid(p.nblk, p.B * p.H);
+  // with the K sums, pass 1 covers every Q block; without them, q_nblk blocks from q_blk0
+  const int qn = part.k_sums ? p.nblk : min(part.q_nblk, p.nblk - part.q_blk0);
+  const dim3 grid1(part.k_sums ? p.nblk : qn, p.B * p.H, part.k_sums ? 2 : 1);
   if (p.qk_mx) {
-    hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16, true>), dim3(p.nblk, p.B * p.H, 2), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16, true>), grid, dim3(kThreads), 0, st, a);
+    if (qn > 0) hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16, true>), grid1, dim3(kThreads), 0, st, a);
+    if (part.k_sums) hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
+    if (part.k_codes) hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16, true>), grid, dim3(kThreads), 0, st, a);
   } else {
-    hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16, false>), dim3(p.nblk, p.B * p.H, 2), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16, false>), grid, dim3(kThreads), 0, st, a);
+    if (qn > 0) hipLaunchKernelGGL((q_quant_k_sums_kernel<D, BF16, false>), grid1, dim3(kThreads), 0, st, a);
+    if (part.k_sums) hipLaunchKernelGGL((k_mean_kernel<D>), dim3(D / 32, p.B * p.H), dim3(256), 0, st, a);
+    if (part.k_codes) hipLaunchKernelGGL((k_quant_bias_kernel<D, BF16, false>), grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -815,9 +830,13 @@ hipError_t quant_v_impl(const Problem& p, TensorView v, const sage_v_buffers& ou
 }  // namespace
 
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
-                           hipStream_t st) {
-  if (p.D == 128) return p.bf16 ? quant_qk_impl<128, true>(p, q, k, out, st) : quant_qk_impl<128, false>(p, q, k, out, st);
-  return p.bf16 ? quant_qk_impl<64, true>(p, q, k, out, st) : quant_qk_impl<64, false>(p, q, k, out, st);
+                           hipStream_t st, const QKPart& part) {
+  if (part.bias && !part.k_codes) return hipErrorInvalidValue;   // the bias is written by the K-code kernel
+  if (p.D == 128)
+    return p.bf16 ? quant_qk_impl<128, true>(p, q, k, out, st, part)
+                  : quant_qk_impl<128, false>(p, q, k, out, st, part);
+  return p.bf16 ? quant_qk_impl<64, true>(p, q, k, out, st, part)
+                : quant_qk_impl<64, false>(p, q, k, out, st, part);
 }
 
 hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st) {

@@ -330,7 +330,15 @@ SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void
   if ((e = sage::launch_quant_qk(pr8, qv, kv, *qk, hs)) != hipSuccess ||
       (e = sage::launch_attn_fwd(pr8, *qk, *vb, causal, o8, os, hs, qb)) != hipSuccess)
     return launch_result(e, "sage_probe_qk_bits (INT8 pass)");
-  if ((e = sage::launch_quant_qk(pr4, qv, kv, *qk, hs)) != hipSuccess ||
+  // The INT4-range pass needs new K codes and the probed Q block's codes only:
+  // the K means and the bias do not depend on the precision, and the INT8
+  // pass's stay valid.
+  sage::QKPart block_only;
+  block_only.bias = false;
+  block_only.k_sums = false;
+  block_only.q_blk0 = qb;
+  block_only.q_nblk = 1;
+  if ((e = sage::launch_quant_qk(pr4, qv, kv, *qk, hs, block_only)) != hipSuccess ||
       (e = sage::launch_attn_fwd(pr4, *qk, *vb, causal, o4, os, hs, qb)) != hipSuccess)
     return launch_result(e, "sage_probe_qk_bits (INT4-range pass)");
   if ((e = sage::launch_probe_reference(pr8, qv, kv, vv, causal, qb, base, hs)) != hipSuccess ||
@@ -348,8 +356,16 @@ SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void
   r.rel_l1_int4 = sums[5] / sums[7];
   r.rel_l1_int8 = sums[6] / sums[7];
   r.qk_bits = r.cos_int4 >= static_cast<double>(cos_min) ? 4 : 8;
-  if (r.qk_bits == 8 && (e = sage::launch_quant_qk(pr8, qv, kv, *qk, hs)) != hipSuccess)
-    return launch_result(e, "sage_probe_qk_bits (INT8 codes)");
+  // Leave the chosen precision's codes: INT8 needs its K codes and the probed
+  // Q block back; INT4-range needs the Q codes of every block.
+  sage::QKPart rest = block_only;
+  if (r.qk_bits == 4) {
+    rest.k_codes = false;
+    rest.q_blk0 = 0;
+    rest.q_nblk = 1 << 30;
+  }
+  if ((e = sage::launch_quant_qk(r.qk_bits == 8 ? pr8 : pr4, qv, kv, *qk, hs, rest)) != hipSuccess)
+    return launch_result(e, "sage_probe_qk_bits (chosen codes)");
   *result = r;
   return ok();
 }

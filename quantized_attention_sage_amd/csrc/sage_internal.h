@@ -29,8 +29,19 @@ struct Problem {
                                  // FP6 E2M3 (SAGE_QK_INT_E2M3); 0: int8
 };
 
+// Parts of sage_quant_qk to run; the default is all of it.  The parts left out
+// keep what the buffers hold, which is only valid when an earlier call on the
+// same inputs wrote them: the K means and the bias do not depend on the code
+// precision (they come from the smoothed K and the Q block means).
+struct QKPart {
+  bool bias = true;      // the bias (needs k_codes)
+  bool k_sums = true;    // the K block sums and K means (and then every Q block)
+  bool k_codes = true;   // the K codes and scales
+  int q_blk0 = 0;        // without k_sums: the Q blocks [q_blk0, q_blk0 + q_nblk)
+  int q_nblk = 1 << 30;
+};
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
-                           hipStream_t st);
+                           hipStream_t st, const QKPart& part = QKPart());
 hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st);
 // probe_qb >= 0 runs only query block probe_qb of every head (B*H work-groups).
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,

@@ -10,7 +10,8 @@ library's own full-tensor path:
   * cosine similarity within 1e-4 and relative L1 within 1e-3 of the oracle's
     probe, and the same choice wherever the oracle's cos_int4 is not within
     1e-4 of cos_min;
-  * on return the workspace holds the codes of the chosen precision.
+  * on return the workspace holds the codes, scales, means and bias of the
+    chosen precision, bit for bit as a fresh quantisation writes them.
 """
 import numpy as np
 import pytest
@@ -54,7 +55,8 @@ def test_probe(case):
     res = api.probe_qk_bits(qt, kt, vt, params, ws, shape, causal, qb, cos_min, scratch)
     torch.cuda.synchronize()
     ref, o4, o8 = (x.float().cpu().numpy() for x in scratch.rows())
-    codes_after = ws.view("k_codes").cpu().numpy().view(np.uint8).copy()
+    names = ("q_codes", "q_scale", "q_mean", "k_codes", "k_scale", "k_mean", "bias")
+    after = {n: ws.view(n).cpu().numpy().copy() for n in names}
     rows = adaptive.probe_rows(w.N, qb)
     nr = len(rows)
 
@@ -76,8 +78,10 @@ def test_probe(case):
         full = out.float().cpu().numpy()[:, :, rows]
         np.testing.assert_array_equal(got[:, :, :nr], full, err_msg=f"INT{bits} rows differ from the full call")
         if bits == res["qk_bits"]:
-            np.testing.assert_array_equal(codes_after, ws2.view("k_codes").cpu().numpy().view(np.uint8),
-                                          err_msg="workspace does not hold the chosen codes")
+            # codes, scales, means and the bias (kept from the probe's first pass) as a fresh quantisation writes them
+            for n in names:
+                np.testing.assert_array_equal(after[n].view(np.uint8), ws2.view(n).cpu().numpy().view(np.uint8),
+                                              err_msg=f"workspace {n} differs from the chosen precision's")
 
     # metrics and choice against the oracle
     want = adaptive.probe_qk_bits(q, k, v, w.dtype, causal, qb, cos_min, gran=w.gran, qk4_format=fmt4)
