@@ -13,14 +13,19 @@ on the codes produced by ``oracle.quant``:
     (steps wholly above the diagonal are skipped when causal):
       s    = (S_int * dQ_i * dK_j + dS_j) * sm_scale * log2(e)   (fp64 -> fp32)
       s    = -inf for padded keys (j >= N) and, when causal, for j > i
-      ms   = max_j s over the step
-      m'   = ms if ms > m + tau else m        (reference maximum, lags by <= tau)
+      m'   = max(m, max_j s)                  (the running row maximum)
       alpha = 2^(m - m')                      (1 when m' = m, 0 while m = -inf)
-      P~   = 2^(s - m')  in (0, 2^tau]         (fp64 -> fp32)
-      p^   = E4M3(P~ * P_r / 2^tau)           (the fixed per-block scale)
-      l    = alpha * l + sum_j P~_j * P_r / 2^tau   (row sum of the fp32 P~)
+      P~   = 2^(s - m')  in (0, 1]             (fp64 -> fp32)
+      p^   = E4M3(P~ * P_r)                   (the fixed per-block scale 1/P_r)
+      l    = alpha * l + sum_j P~_j * P_r     (row sum of the fp32 P~)
       acc  = alpha * acc + sum_j dec(p^_j) * dec(v^_j)
     O = acc * dV / l + mu_V, rounded once to the output dtype.
+
+This is the textbook online softmax: the reference maximum is the running
+maximum, and every P~ of a step is formed against the maximum of all scores
+seen so far.  (``tau`` > 0 is an analysis option only: the reference may then
+lag the running maximum by up to tau, m' = ms only if ms > m + tau, and
+P~ <= 2^tau is encoded as E4M3(P~ * P_r / 2^tau).  The library does not use it.)
 
 With MXFP4 Q and K (qk["qk_format"] = "mxfp4", the FP4 microscaling of the
 SageAttention3 abstract read as OCP MXFP4, see oracle.fp4) the codes carry
@@ -32,15 +37,16 @@ the setting the SageAttention2 abstract starts from) the V codes are V itself,
 P~ = 2^(s - m') is rounded to that type with ties to even instead of being
 scaled and encoded to E4M3, and l sums the fp32 P~ as before.
 
-With tau = 0 this is textbook online softmax (the reference maximum is the
-running maximum).  tau > 0 lets the reference lag the running maximum by up
-to tau (P~ <= 2^tau), which skips most O rescales.  The library's kernel uses
-BK = 128 and tau = 4 and sums the fp32 P~ (``l_fp8=False``, the plain
-FlashAttention reading); ``l_fp8=True`` sums the FP8-rounded P~ instead,
-which makes O an exactly normalised weighted average of the V codes.
-Everything except the fp32 values that decide an E4M3 code is float64.  The
-reference maximum changes per step, so the emulated P~ depends on BK and tau;
-both must equal the kernel's.
+``codecs`` switches the three quantisers independently (the pins use it):
+"qk" (integer / MXFP4 Q and K codes with their scales; off: the smoothed fp32
+Q', K' with unit scales), "p" (P~ to E4M3 or to the 16-bit type; off: the
+fp32 P~ itself) and "v" (V' to E4M3 with per-channel scales; off: the
+smoothed fp32 V').  With none of them the result must equal exact attention
+up to fp32 rounding of s and P~.  l sums the fp32 P~ (``l_fp8=False``, the
+plain FlashAttention reading); ``l_fp8=True`` sums the rounded P~ instead, an
+alternative reading that is not used.  Everything except the fp32 values that
+decide a code is float64.  The running maximum changes per step, so the
+emulated P~ depends on BK, which must equal the kernel's key tile (128).
 """
 from __future__ import annotations
 
@@ -54,7 +60,8 @@ from .quant import QBLOCK, q_group_index, k_group_index, bias_row
 
 LOG2E = 1.0 / math.log(2.0)
 DEFAULT_BK = 128
-DEFAULT_TAU = 4.0
+DEFAULT_TAU = 0.0
+ALL_CODECS = frozenset(("qk", "p", "v"))
 
 
 def round16(x: np.ndarray, kind: str) -> np.ndarray:
@@ -108,59 +115,68 @@ def exact_attention(q, k, v, causal=False, sm_scale=None, row_block=256):
 
 def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_scale=None,
                   p_range: float = 448.0, bk: int = DEFAULT_BK, quantized: bool = True,
-                  tau: float = DEFAULT_TAU, l_fp8: bool = False):
+                  tau: float = DEFAULT_TAU, l_fp8: bool = False, codecs=None, trace=None):
     """Emulate one 128-query block; returns (O float64 [rows, d], rows).
 
-    ``quantized=False`` switches every quantiser off (identity codecs: the
-    smoothed fp32 values stand for the codes, scales are 1 and P~ is not
-    rounded to FP8); the result must then equal exact attention up to fp32
-    rounding of s and P~, which pins the tiling, the online softmax and the
-    smoothing add-backs.
+    ``codecs`` (a subset of {"qk", "p", "v"}) picks the quantisers that run;
+    by default all of them when ``quantized`` and none otherwise.  With none
+    the smoothed fp32 values stand for the codes, scales are 1 and P~ is not
+    rounded, so the result must equal exact attention up to fp32 rounding of s
+    and P~, which pins the tiling, the online softmax and the smoothing
+    add-backs.  ``trace``, a list, receives one dict per key step with the
+    step's running maximum ``m``, the fp32 ``P`` (P~ times the code scale),
+    the weights ``w`` that multiply V (decoded P~ codes), ``alpha`` and ``l``.
     """
+    codecs = (ALL_CODECS if quantized else frozenset()) if codecs is None else frozenset(codecs)
+    if not codecs <= ALL_CODECS:
+        raise ValueError(f"unknown codecs {sorted(codecs - ALL_CODECS)}")
     N, n_pad = qk["N"], qk["n_pad"]
     d = qk["k_mean"].shape[-1]
     scale = _default_scale(d, sm_scale) * LOG2E
     q0 = qb * QBLOCK
     nrows = min(QBLOCK, N - q0)
     qi = q0 + np.arange(QBLOCK)
-    if quantized:
-        if qk.get("qk_format", "int") == "mxfp4":
-            # MXFP4 codes carry their block scales: S is the exact dot product of the decoded rows
-            qmat = qk["q_values"][b, h, q0:q0 + QBLOCK]
-            dq = np.ones(QBLOCK)
-            kmat = qk["k_values"][b, h]
-            dk = np.ones(n_pad)
-        else:
-            if qk.get("qk_format", "int") == "int_e4m3":
-                # integer codes held as E4M3 bytes: decode to the same integers
-                qmat = e4m3_decode(qk["q_codes"][b, h, q0:q0 + QBLOCK])
-                kmat = e4m3_decode(qk["k_codes"][b, h])
-            elif qk.get("qk_format", "int") == "int_e2m3":
-                # integer codes held as packed E2M3: unpack and decode to the same integers
-                qmat = e2m3_decode(unpack_slots(qk["q_codes"][b, h, q0:q0 + QBLOCK]))
-                kmat = e2m3_decode(unpack_slots(qk["k_codes"][b, h]))
-            else:
-                qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
-                kmat = qk["k_codes"][b, h].astype(np.float64)
-            dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
-            dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
-        pv16 = vq.get("pv", "fp8") != "fp8"
-        if pv16:
-            vmat = vq["v_values"][b, h].astype(np.float64)
-            pscale = 1.0
-        else:
-            vmat = e4m3_decode(vq["v_codes"][b, h])
-            pscale = float(np.float32(p_range)) * 2.0 ** -tau     # E4M3 code of P~ = E4M3(P~ * pscale)
-        dv = vq["v_scale"][b, h].astype(np.float64)
-    else:
-        pv16 = vq.get("pv", "fp8") != "fp8"
+    fmt = qk.get("qk_format", "int")
+    if "qk" not in codecs:
         qmat = qk["q_smoothed"][b, h, q0:q0 + QBLOCK].astype(np.float64)
         dq = np.ones(QBLOCK)
         kmat = qk["k_smoothed"][b, h].astype(np.float64)
         dk = np.ones(n_pad)
-        vmat = vq["v_smoothed"][b, h].astype(np.float64)
+    elif fmt == "mxfp4":
+        # MXFP4 codes carry their block scales: S is the exact dot product of the decoded rows
+        qmat = qk["q_values"][b, h, q0:q0 + QBLOCK]
+        dq = np.ones(QBLOCK)
+        kmat = qk["k_values"][b, h]
+        dk = np.ones(n_pad)
+    else:
+        if fmt == "int_e4m3":
+            # integer codes held as E4M3 bytes: decode to the same integers
+            qmat = e4m3_decode(qk["q_codes"][b, h, q0:q0 + QBLOCK])
+            kmat = e4m3_decode(qk["k_codes"][b, h])
+        elif fmt == "int_e2m3":
+            # integer codes held as packed E2M3: unpack and decode to the same integers
+            qmat = e2m3_decode(unpack_slots(qk["q_codes"][b, h, q0:q0 + QBLOCK]))
+            kmat = e2m3_decode(unpack_slots(qk["k_codes"][b, h]))
+        else:
+            qmat = qk["q_codes"][b, h, q0:q0 + QBLOCK].astype(np.float64)
+            kmat = qk["k_codes"][b, h].astype(np.float64)
+        dq = qk["q_scale"][b, h][q_group_index(n_pad, qk["gran"])[q0:q0 + QBLOCK]].astype(np.float64)
+        dk = qk["k_scale"][b, h][k_group_index(n_pad, qk["gran"])].astype(np.float64)
+    pv16 = vq.get("pv", "fp8") != "fp8"
+    if pv16:
+        # 16-bit P~V: V is used as given (v_values; its scale is 1 and its mean 0)
+        vmat = vq["v_values"][b, h].astype(np.float64)
         dv = np.ones(d)
         pscale = 1.0
+    else:
+        if "v" in codecs:
+            vmat = e4m3_decode(vq["v_codes"][b, h])
+            dv = vq["v_scale"][b, h].astype(np.float64)
+        else:
+            vmat = vq["v_smoothed"][b, h].astype(np.float64)
+            dv = np.ones(d)
+        # the E4M3 code of P~ is E4M3(P~ * pscale): the fixed scale 1 / P_r
+        pscale = float(np.float32(p_range)) * 2.0 ** -tau if "p" in codecs else 1.0
     bias = (qk["bias"][b, h, qb] if qk.get("bias") is not None else bias_row(qk, b, h, qb)).astype(np.float64)
 
     key_end = min(N, q0 + QBLOCK) if causal else N
@@ -179,22 +195,25 @@ def emulate_block(qk: dict, vq: dict, b: int, h: int, qb: int, causal: bool, sm_
         alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - np.where(np.isneginf(m_new), 0.0, m_new)))
         base = np.where(np.isneginf(m_new), 0.0, m_new)
         P = np.exp2(s.astype(np.float64) - base[:, None]).astype(np.float32)
-        if pv16:
+        PS = (P * np.float32(pscale)).astype(np.float32)               # P~ times the code scale (exact when 1)
+        if "p" not in codecs:
+            pw = PS.astype(np.float64)
+        elif pv16:
             pw = round16(P, vq["pv"])
-        elif quantized:
-            pw = e4m3_decode(e4m3_encode((P * np.float32(pscale)).astype(np.float32)))
         else:
-            pw = P.astype(np.float64)
+            pw = e4m3_decode(e4m3_encode(PS))
         l = alpha * l + (pw.sum(axis=1) if l_fp8 else P.astype(np.float64).sum(axis=1) * pscale)
         acc = alpha[:, None] * acc + pw @ vmat[j]
         m = m_new
+        if trace is not None:
+            trace.append(dict(keys=j, m=m.copy(), P=PS.copy(), w=pw.copy(), alpha=alpha.copy(), l=l.copy()))
     o = acc * dv[None, :] / l[:, None] + vq["v_mean"][b, h].astype(np.float64)[None, :]
     return o[:nrows], qi[:nrows]
 
 
 def emulate_attention(qk: dict, vq: dict, causal: bool, sm_scale=None, p_range: float = 448.0,
                       bk: int = DEFAULT_BK, quantized: bool = True, blocks=None,
-                      tau: float = DEFAULT_TAU, l_fp8: bool = False):
+                      tau: float = DEFAULT_TAU, l_fp8: bool = False, codecs=None):
     """Emulate the whole tensor (or the (b, h, qb) triples in ``blocks``).
 
     Returns float64 [B,H,N,d] (rows of blocks not asked for are NaN).
@@ -206,7 +225,7 @@ def emulate_attention(qk: dict, vq: dict, causal: bool, sm_scale=None, p_range: 
     if blocks is None:
         blocks = [(b, h, qb) for b in range(B) for h in range(H) for qb in range(n_pad // QBLOCK)]
     for (b, h, qb) in blocks:
-        o, rows = emulate_block(qk, vq, b, h, qb, causal, sm_scale, p_range, bk, quantized, tau, l_fp8)
+        o, rows = emulate_block(qk, vq, b, h, qb, causal, sm_scale, p_range, bk, quantized, tau, l_fp8, codecs)
         out[b, h, rows] = o
     return out
 

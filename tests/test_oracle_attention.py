@@ -240,7 +240,7 @@ def _pv16_error(kind, causal, name="image_dit", N=300):
     p = QuantParams(pv=kind)
     qk, vq = oracle.quant_qk(q, k, p), oracle.quant_v(v, p)
     ex = oracle.exact_attention(q, k, v, causal)
-    em = oracle.emulate_attention(qk, vq, causal, quantized=False)
+    em = oracle.emulate_attention(qk, vq, causal, codecs={"p"})     # QK quantisation off, P~ rounded
     return np.abs(em - ex).max() / np.abs(v).max()
 
 
