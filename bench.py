@@ -8,8 +8,9 @@ synthetic inputs already resident in HBM.  Prints ONE JSON line.  `value` is
 attention TOPS of the whole step: 4*B*H*N^2*d (halved when causal) divided by
 the step time.  `roofline` covers the attention kernel, timed with HIP events
 on the stream it is launched on.  `cpu_baseline` times the CPU oracle
-(quantisation emulation plus tiled attention emulation) on a bounded sample of
-the same workload and extrapolates per head.
+(quantisation emulation plus tiled attention emulation, and exact fp64
+attention) on a bounded sample of the same workload and extrapolates it;
+`accuracy` compares the GPU output with both on those sampled rows.
 """
 from __future__ import annotations
 
@@ -76,45 +77,119 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, sample_blocks: int = 96, pv: str = "fp8", qk_format: str = "int"):
-    """Time the oracle on one head: quantisation of the head plus the tiled
-    emulation of `sample_blocks` query blocks, extrapolated to the workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _emulate_head(job):
+    """One worker of the emulation timing: the oracle's quantisation of one head
+    plus the tiled emulation of the given query blocks (one BLAS thread)."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     import oracle
     from oracle.quant import QuantParams
-    from quantized_attention_sage_amd.workloads import make_inputs, scaled
+    q, k, v, params, blocks, causal = job
+    with threadpool_limits(1):
+        p = QuantParams(**params)
+        t0 = time.perf_counter()
+        qk = oracle.quant_qk(q, k, p, with_bias=False)
+        vq = oracle.quant_v(v, p)
+        t_quant = time.perf_counter() - t0
+        outs = []
+        t0 = time.perf_counter()
+        for qb in blocks:
+            o, rows = oracle.emulate_block(qk, vq, 0, 0, qb, causal)
+            outs.append(o)
+        t_blocks = time.perf_counter() - t0
+    return t_quant, t_blocks, np.concatenate(outs)
 
-    one = scaled(w, B=1, H=1)
-    q, k, v = make_inputs(one)
-    p = QuantParams(qk_bits=w.qk_bits, gran=w.gran, pv=w.dtype if pv == "f16" else "fp8", qk_format=qk_format)
+
+def cpu_baseline(w, q, k, v, out_gpu, pv: str = "fp8", qk_format: str = "int", blocks_per_head: int = 12):
+    """Time the oracle (as it stands) on a bounded sample of the workload, on the
+    host's cores, and compare the GPU output with it on the same rows.
+
+    Sample: P heads spread over B*H (P = worker processes, at most 16) and
+    `blocks_per_head` query blocks spread over each head's blocks.
+      * emulation (the quantised method): one process per head, each running
+        the oracle's quantisation of its head and the tiled emulation of its
+        blocks; extrapolated to B*H heads x all blocks at P heads in parallel;
+      * exact fp64 attention of the same rows through BLAS on all P cores,
+        extrapolated the same way.
+    The GPU output of those rows is then checked against both (the accuracy of
+    the measured line: cosine similarity and relative L1 against exact
+    attention, the metrics of the SageAttention2++ summary's "A.2 Datasets and
+    Metrics"; max |O - emulation| against the 2e-3 max|V| bar)."""
+    import multiprocessing as mp
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    nqb = -(-w.N // 128)
+    heads = sorted(set(int(x) for x in np.linspace(0, w.B * w.H - 1, min(cores, w.B * w.H))))
+    picks = sorted(set(int(x) for x in np.linspace(0, nqb - 1, min(blocks_per_head, nqb))))
+    params = dict(qk_bits=w.qk_bits, gran=w.gran, pv=w.dtype if pv == "f16" else "fp8", qk_format=qk_format)
+    jobs = []
+    for bh in heads:
+        b, h = divmod(bh, w.H)
+        jobs.append((q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], params, picks, w.causal))
+    ctx = mp.get_context("spawn")   # workers touch no GPU state and start from a clean interpreter
     t0 = time.perf_counter()
-    qk = oracle.quant_qk(q, k, p, with_bias=False)
-    vq = oracle.quant_v(v, p)
-    t_quant = time.perf_counter() - t0
-    nqb = qk["n_pad"] // 128
-    picks = sorted(set(int(x) for x in np.linspace(0, nqb - 1, sample_blocks)))
+    with ctx.Pool(len(jobs)) as pool:
+        res = pool.map(_emulate_head, jobs)
+    wall_emul = time.perf_counter() - t0
+
+    keys = [min(w.N, 128 * (qb + 1)) if w.causal else w.N for qb in picks]
+    mean_keys = (sum(min(w.N, 128 * (b + 1)) for b in range(nqb)) / nqb) if w.causal else w.N
+    # per head: quantisation + every block at the sampled per-key cost; heads run P at a time
+    per_head = [tq + tb / sum(keys) * mean_keys * nqb for (tq, tb, _) in res]
+    t_emul = float(np.mean(per_head)) * (w.B * w.H) / len(jobs)
+
+    rows = np.concatenate([np.arange(128 * qb, min(w.N, 128 * qb + 128)) for qb in picks])
+    ex_rows = []
     t0 = time.perf_counter()
-    for qb in picks:
-        oracle.emulate_block(qk, vq, 0, 0, qb, w.causal)
-    t_blocks = time.perf_counter() - t0
-    if w.causal:   # block cost grows with its key count; scale by the mean over blocks
-        keys = [min(w.N, 128 * (qb + 1)) for qb in picks]
-        mean_keys = sum(min(w.N, 128 * (b + 1)) for b in range(nqb)) / nqb
-        per_block = t_blocks / sum(keys) * mean_keys
-    else:
-        per_block = t_blocks / len(picks)
-    t_total = w.B * w.H * (t_quant + nqb * per_block)
-    threads = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max(blas) if blas else threads
-    except Exception:
-        pass
-    return {"value": w.ops / t_total / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": (f"one head of {w.name}: oracle quantisation of Q,K,V ({t_quant:.2f}s) + tiled emulation of "
-                       f"query blocks {picks} ({t_blocks:.2f}s), extrapolated to B*H heads x {nqb} blocks"),
-            "seconds_measured": round(t_quant + t_blocks, 2), "seconds_extrapolated": round(t_total, 1)}
+    with threadpool_limits(cores):
+        for bh in heads:
+            b, h = divmod(bh, w.H)
+            ex_rows.append(oracle.exact_attention_rows(q[b, h], k[b, h], v[b, h], rows, w.causal))
+    t_exact_s = time.perf_counter() - t0
+    # exact attention costs the same for every row (all N keys, masked when causal)
+    t_exact = t_exact_s * (w.B * w.H * w.N) / (len(heads) * len(rows))
+
+    gpu = np.concatenate([out_gpu[divmod(bh, w.H)][rows] for bh in heads]).astype(np.float64)
+    ex = np.concatenate(ex_rows)
+    em = np.concatenate([r[2] for r in res])
+    cos = float((gpu.ravel() @ ex.ravel()) / (np.linalg.norm(gpu) * np.linalg.norm(ex)))
+    rl1 = float(np.abs(gpu - ex).sum() / np.abs(ex).sum())
+    cos_e = float((em.ravel() @ ex.ravel()) / (np.linalg.norm(em) * np.linalg.norm(ex)))
+    rl1_e = float(np.abs(em - ex).sum() / np.abs(ex).sum())
+    tol = 2e-3 * float(np.abs(v).max())
+    accuracy = {
+        "rows": f"query blocks {picks} of heads {heads} ({len(rows) * len(heads)} rows)",
+        "vs_exact": {"cos": round(cos, 6), "rel_l1": round(rl1, 5),
+                     "bar": {"cos": 0.999, "rel_l1": 0.02}, "met": bool(cos >= 0.999 and rl1 <= 0.02)},
+        "emulation_vs_exact": {"cos": round(cos_e, 6), "rel_l1": round(rl1_e, 5)},
+        "vs_emulation": {"max_abs_err": float(np.abs(gpu - em).max()), "tol": tol,
+                         "frac_of_tol": round(float(np.abs(gpu - em).max()) / tol, 4)},
+    }
+    base = {"value": w.ops / t_emul / 1e12, "unit": "TOPS", "cores": len(jobs), "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": (f"{w.name}: heads {heads} (one process each, one BLAS thread) x query blocks {picks}: "
+                       f"oracle quantisation of the head + tiled emulation of the blocks "
+                       f"({wall_emul:.1f}s wall), extrapolated to {w.B * w.H} heads x {nqb} blocks"),
+            "seconds_measured": round(wall_emul, 2), "seconds_extrapolated": round(t_emul, 1),
+            "exact_fp64": {"value": w.ops / t_exact / 1e12, "unit": "TOPS", "cores": cores,
+                           "sample": f"exact fp64 attention of the same {len(rows) * len(heads)} rows through BLAS "
+                                     f"({t_exact_s:.1f}s), extrapolated to the workload",
+                           "seconds_measured": round(t_exact_s, 2), "seconds_extrapolated": round(t_exact, 1)}}
+    return base, accuracy
 
 
 def probe_bench(args, w, qt, kt, vt, shape, ws, dev):
@@ -185,7 +260,6 @@ def main():
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
     q, k, v = make_inputs(w)
     qt, kt, vt = (torch.from_numpy(x).to(tdt).to(dev) for x in (q, k, v))
-    del q, k, v
     params = api.make_params(qk_bits=w.qk_bits, gran=w.gran, pv=args.pv, qk_format=args.qk)
     shape = api.make_shape(qt, kt, vt)
     ws = api.Workspace(shape, params, dev)
@@ -280,8 +354,12 @@ def main():
                         "frac": round(v_bytes / (v_ms * 1e6) / PEAK_HBM_GBPS, 4)},
         },
     }
+    rec["accuracy"] = None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, pv=args.pv, qk_format=args.qk)
+        step()
+        torch.cuda.synchronize()
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline(w, q, k, v, out.float().cpu().numpy(), pv=args.pv,
+                                                            qk_format=args.qk)
     print(json.dumps(rec), flush=True)
 
 

@@ -23,10 +23,10 @@
 //    matrix-core work is interleaved with its own vector work: tile t's
 //    dequantisation and row maximum run beside the PV product of tile t-1,
 //    and tile t's exp2 / FP8 packing beside the QK product of tile t+1.
-//  * online softmax against a reference maximum that may lag the running
-//    maximum by up to TAU (log2 units): the reference moves, and O is
-//    rescaled, only when a tile's maximum exceeds it by more than TAU.  P~ is
-//    then at most 2^TAU and is encoded as E4M3(P~ * P_r / 2^TAU).
+//  * online softmax against the running row maximum m (log2 units): P~ =
+//    2^(s - m) <= 1 is encoded as E4M3(P~ * P_r); O and l are rescaled when
+//    some row of the wave has a new maximum (the rescale is skipped, exactly,
+//    when none has).
 //  * K codes, V codes and each tile's bias row and K scales are copied straight
 //    from global memory into two-slot LDS rings, one tile ahead of their use.
 #include "sage_internal.h"
@@ -41,7 +41,6 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 128;        // keys per tile (one online-softmax update)
-constexpr float kTau = 4.0f;      // allowed lag of the reference maximum (log2 units)
 
 struct AttnArgs {
   const int8_t* q_codes;
@@ -58,7 +57,8 @@ struct AttnArgs {
   float scale_log2;  // sm_scale * log2(e)
   float log2_pr;     // log2(P_r)
   int lpt_g;         // causal: heads per longest-first group (map_block)
-  int probe_qb;      // PROBE kernels: the one query block of every head (work-group id = head)
+  int probe_qb;      // PROBE kernels: the one query block of every head (work-group id = head);
+                     // their output row of query i is i - 128 probe_qb ([B, H, 128, d] spans)
 };
 
 // 16-byte chunk swizzle inside a tile row so that the 16 lanes served together
@@ -137,11 +137,11 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
 // publishes them.  The "memory" clobber keeps LDS reads on their side.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 
 // Sources of the tile copies.  With chunk p = 256 j + threadIdx.x the swizzled
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     dq = a.q_scale[static_cast<int64_t>(bh) * a.nblk + qb];
   }
   const float dq2 = dq * a.scale_log2;
-  // exp2(x - (m + base_shift)) = P~ * P_r / 2^TAU with P~ = exp2(x - m)
-  const float base_shift = kTau - a.log2_pr;
+  // exp2(x - (m + base_shift)) = P~ * P_r with P~ = exp2(x - m)
+  const float base_shift = -a.log2_pr;
   const bool thread_gran = a.gran == SAGE_GRAN_THREAD;
 
   // First key of tile u; tiles past the end copy the last tile again (their
@@ -400,10 +400,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
                   __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_slot)::value, NXT = 1 - CUR;
     const int k0 = tt * kTile;
-    // This wave's copies of aux(t) (issued when tile t-1 started) and of V(t)
-    // are complete; only the 2J copies of K(t+1) and V(t) issued in phase B of
-    // tile t-1... (see the mid-tile wait) may still run.  After the barrier
-    // every wave is done with aux(t-1), whose slot is refilled below.
+    // This wave's copy of aux(t) (issued when tile t-1 started) is complete:
+    // only the 2J copies of K(t+1) and V(t), issued after it in phase B of tile
+    // t-1, may still run (vector memory loads return in issue order, so the
+    // count bounds the oldest).  K(t+1) is waited for at the mid-tile wait,
+    // V(t) at the next tile's.  After the barrier every wave is done with
+    // aux(t-1), whose slot is refilled below.
     if constexpr (J == 4) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     copy_aux(lds0 + R::A0 + NXT * R::AUX, src, thread_gran, kofs(tt + 1), w);
@@ -502,11 +504,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         }
     }
     const float mt = fmaxf(mx, __shfl_xor(mx, 32));
-    // The reference maximum moves only when this tile's maximum exceeds it by more than TAU.
-    const float mnew = mt > m + kTau ? mt : m;
+    // Running maximum: P~ of this tile is formed against max(m, tile maximum).
+    const float mnew = mt > m ? mt : m;
     const float alpha = (m == mnew) ? 1.f : ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
     const float base = (mnew == -INFINITY) ? 0.f : mnew + base_shift;
-    // Exact skip: alpha == 1 for every row of this wave unless a reference moved.
+    // Exact skip: alpha == 1 for every row of this wave unless a running maximum moved.
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
@@ -591,7 +593,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const float inv = 1.f / ltot;
   if (qi < a.N) {
     const int b = bh / a.H, h = bh % a.H;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.oB + h * a.oH + static_cast<int64_t>(qi) * a.oN;
+    const int orow_i = PROBE ? qi - q0 : qi;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.oB + h * a.oH + static_cast<int64_t>(orow_i) * a.oN;
     const float* vsc = a.v_scale + static_cast<int64_t>(bh) * D;
     const float* vmn = a.v_mean + static_cast<int64_t>(bh) * D;
 #pragma unroll

@@ -6,7 +6,7 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands: each lane's 32 codes of
 // a 64-channel step come with the E8M0 scale of its 32-channel block, and the
 // product arrives in fp32 with the scales applied.  The rest (smoothing bias,
-// lagged online softmax, FP8 P~ and V, epilogue) is the FP8 kernel of
+// online softmax, FP8 P~ and V, epilogue) is the FP8 kernel of
 // attn.hip, whose schedule this file keeps.  What differs:
 //  * dequantisation is one FMA per score (s = S sm_scale log2 e + bias): no
 //    integer-to-float conversion and no per-group scales;
@@ -25,7 +25,6 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 128;        // keys per tile (one online-softmax update)
-constexpr float kTau = 4.0f;      // allowed lag of the reference maximum (log2 units)
 
 struct AttnArgs {
   const int8_t* q_codes;
@@ -123,11 +122,11 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
 // publishes them.  The "memory" clobber keeps LDS reads on their side.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 
 // Sources of the tile copies.  With chunk p = 256 j + threadIdx.x the swizzled
@@ -246,8 +245,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
     }
   }
   const float c_log2 = a.scale_log2;
-  // exp2(x - (m + base_shift)) = P~ * P_r / 2^TAU with P~ = exp2(x - m)
-  const float base_shift = kTau - a.log2_pr;
+  // exp2(x - (m + base_shift)) = P~ * P_r with P~ = exp2(x - m)
+  const float base_shift = -a.log2_pr;
 
   // First key of tile u; tiles past the end copy the last tile again (their
   // data is never used, and every wave keeps one copy count per issue point).
@@ -438,11 +437,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp4_kernel(AttnArgs a) {
         }
     }
     const float mt = fmaxf(mx, __shfl_xor(mx, 32));
-    // The reference maximum moves only when this tile's maximum exceeds it by more than TAU.
-    const float mnew = mt > m + kTau ? mt : m;
+    // Running maximum: P~ of this tile is formed against max(m, tile maximum).
+    const float mnew = mt > m ? mt : m;
     const float alpha = (m == mnew) ? 1.f : ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
     const float base = (mnew == -INFINITY) ? 0.f : mnew + base_shift;
-    // Exact skip: alpha == 1 for every row of this wave unless a reference moved.
+    // Exact skip: alpha == 1 for every row of this wave unless a running maximum moved.
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)

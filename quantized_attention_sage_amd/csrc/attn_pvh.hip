@@ -37,7 +37,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 128;        // keys per tile (one online-softmax update)
-constexpr float kTau = 4.0f;      // allowed lag of the reference maximum (log2 units)
 
 struct AttnArgs {
   const int8_t* q_codes;
@@ -136,11 +135,11 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
 // publishes them.  The "memory" clobber keeps LDS reads on their side.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory");
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 
 // Sources of the tile copies.  With chunk p = 256 j + threadIdx.x the swizzled
@@ -277,8 +276,8 @@ __global__ __launch_bounds__(256, 2) void attn_pvh_kernel(AttnArgs a) {
     dq = a.q_scale[static_cast<int64_t>(bh) * a.nblk + qb];
   }
   const float dq2 = dq * a.scale_log2;
-  // exp2(x - (m + base_shift)) = P~ = exp2(x - m): the host passes log2_pr = TAU
-  const float base_shift = kTau - a.log2_pr;
+  // exp2(x - (m + base_shift)) = P~ = exp2(x - m): the host passes log2_pr = 0
+  const float base_shift = -a.log2_pr;
   const bool thread_gran = a.gran == SAGE_GRAN_THREAD;
 
   // First key of tile u; tiles past the end copy the last tile again (their
@@ -456,11 +455,11 @@ __global__ __launch_bounds__(256, 2) void attn_pvh_kernel(AttnArgs a) {
         }
     }
     const float mt = fmaxf(mx, __shfl_xor(mx, 32));
-    // The reference maximum moves only when this tile's maximum exceeds it by more than TAU.
-    const float mnew = mt > m + kTau ? mt : m;
+    // Running maximum: P~ of this tile is formed against max(m, tile maximum).
+    const float mnew = mt > m ? mt : m;
     const float alpha = (m == mnew) ? 1.f : ((m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew));
     const float base = (mnew == -INFINITY) ? 0.f : mnew + base_shift;
-    // Exact skip: alpha == 1 for every row of this wave unless a reference moved.
+    // Exact skip: alpha == 1 for every row of this wave unless a running maximum moved.
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int c = 0; c < CT; ++c)
@@ -575,7 +574,7 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.gran = p.gran; a.causal = causal ? 1 : 0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   // P~ = 2^(s - m) itself (no E4M3 range to fill): base shift 0.
-  a.log2_pr = kTau;
+  a.log2_pr = 0.f;
   a.lpt_g = lpt_group(p.B * p.H, static_cast<int64_t>(3) * p.n_pad * p.D);
   hipLaunchKernelGGL((attn_pvh_kernel<D, BF16>), dim3(p.nblk * p.B * p.H), dim3(256), 0, st, a);
   return hipGetLastError();

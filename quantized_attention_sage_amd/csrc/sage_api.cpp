@@ -317,13 +317,12 @@ SAGE_API sage_status sage_probe_qk_bits(const void* q, const void* k, const void
   const sage::TensorView kv{k, s->k_stride[0], s->k_stride[1], s->k_stride[2]};
   const sage::TensorView vv{v, s->v_stride[0], s->v_stride[1], s->v_stride[2]};
   char* base = static_cast<char*>(scratch);
-  // outputs [B, H, 128, d]: the kernel writes row q0 + r at o + (q0 + r) * d, so the
-  // pointer handed over sits q0 rows before the span (only rows >= q0 are written)
-  const int64_t D = s->d, q0 = 128 * q_block;
+  // outputs [B, H, 128, d]: the probe instantiation writes query q0 + r of the
+  // block to row r of its head
+  const int64_t D = s->d;
   const int64_t os[3] = {s->H * 128 * D, 128 * D, D};
-  const uintptr_t ub = reinterpret_cast<uintptr_t>(base), shift = static_cast<uintptr_t>(q0 * D * 2);
-  void* o4 = reinterpret_cast<void*>(ub + PL.o4 - shift);
-  void* o8 = reinterpret_cast<void*>(ub + PL.o8 - shift);
+  void* o4 = base + PL.o4;
+  void* o8 = base + PL.o8;
   const int qb = static_cast<int>(q_block);
   hipError_t e;
   if ((e = sage::launch_quant_v(pr8, vv, *vb, hs)) != hipSuccess) return launch_result(e, "sage_probe_qk_bits (quant_v)");

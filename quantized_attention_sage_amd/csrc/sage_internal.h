@@ -43,7 +43,8 @@ struct QKPart {
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
                            hipStream_t st, const QKPart& part = QKPart());
 hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st);
-// probe_qb >= 0 runs only query block probe_qb of every head (B*H work-groups).
+// probe_qb >= 0 runs only query block probe_qb of every head (B*H work-groups)
+// and writes query 128 probe_qb + r of a head to output row r ([B, H, 128, d]).
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb = -1);
 // The same attention with MXFP4 Q and K codes on the scaled FP4 matrix cores (Problem::qk_mx).

@@ -39,22 +39,138 @@ def to_device(x: np.ndarray, dtype: str, layout: str = "bhnd"):
     return t
 
 
+# ------------------------------------------------------------------ guard bands
+# Canary bytes before, between and after every span the library may write; a
+# kernel that writes outside its buffer changes one of them.
+GUARD = 4096          # bytes of canary before the first and after the last span
+CANARY = 0xA5
+OUT_CANARY = 0x7FA5   # 16-bit canary around outputs (a NaN pattern in fp16 and bf16)
+
+
+def _guard_regions(spans, base, total, length):
+    """[lo, hi) byte ranges of a guarded allocation that no span covers."""
+    regions, pos = [(0, base)], base
+    for off, size in sorted(spans):
+        if base + off > pos:
+            regions.append((pos, base + off))
+        pos = max(pos, base + off + size)
+    regions.append((max(pos, base + total), length))
+    return [(lo, hi) for lo, hi in regions if hi > lo]
+
+
+def _check_canary(t, regions, what):
+    for lo, hi in regions:
+        bad = int((t[lo:hi] != CANARY).sum().item())
+        assert bad == 0, f"{what}: {bad} canary bytes overwritten in [{lo}, {hi})"
+
+
+def guarded_workspace(shape, params, device):
+    """A Workspace whose allocation is pre-filled with canary bytes and has a
+    guard band before and after; .check_guards() verifies every byte outside
+    the spans of sage_layout is untouched."""
+    import ctypes
+    import torch
+    from quantized_attention_sage_amd import api, _lib as L
+
+    class GuardedWorkspace(api.Workspace):
+        def __init__(self):
+            lay = L.Layout()
+            L.check(L.lib().sage_workspace_layout(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(lay)))
+            self.layout = lay
+            self.shape = (shape.B, shape.H, shape.N, shape.d)
+            self.pv_f16 = params.pv_mode == L.PV_MODE["f16"]
+            self.qk_mx = params.qk_format == L.QK_FORMAT["mxfp4"]
+            self.qk_held = params.qk_format in (L.QK_FORMAT["int_e4m3"], L.QK_FORMAT["int_e2m3"])
+            self.tensor = torch.full((lay.total_bytes + 2 * GUARD + 256,), CANARY, dtype=torch.uint8, device=device)
+            self._pad = (-self.tensor.data_ptr()) % 256 + GUARD
+            self.qk = L.QKBuffers()
+            self.vb = L.VBuffers()
+            L.check(L.lib().sage_bind_workspace(ctypes.byref(lay), ctypes.c_void_p(self.ptr),
+                                                ctypes.c_size_t(lay.total_bytes), ctypes.byref(self.qk),
+                                                ctypes.byref(self.vb)))
+
+        def check_guards(self):
+            lay = self.layout
+            names = ("q_codes", "q_scale", "q_mean", "k_codes", "k_scale", "k_mean", "bias", "k_partial",
+                     "v_codes", "v_scale", "v_mean", "v_partial")
+            spans = [(getattr(lay, n).offset, getattr(lay, n).bytes) for n in names]
+            _check_canary(self.tensor, _guard_regions(spans, self._pad, lay.total_bytes, self.tensor.numel()),
+                          "workspace")
+
+    return GuardedWorkspace()
+
+
+class GuardedOut:
+    """An output tensor shaped like `like` (contiguous [B,H,N,d]) inside a larger
+    allocation whose ends hold a 16-bit canary."""
+
+    def __init__(self, like, guard_elems=GUARD // 2):
+        import torch
+        n = like.numel()
+        self.g = guard_elems
+        self.buf = torch.full((n + 2 * guard_elems,), OUT_CANARY, dtype=torch.int16, device=like.device)
+        self.out = self.buf[guard_elems:guard_elems + n].view(like.dtype).view(like.shape)
+
+    def check(self):
+        for part in (self.buf[:self.g], self.buf[-self.g:]):
+            bad = int((part != OUT_CANARY).sum().item())
+            assert bad == 0, f"output guard: {bad} canary elements overwritten"
+
+
+def guarded_probe_scratch(shape, device):
+    """A ProbeScratch pre-filled with canary bytes, with a guard band before and
+    after, and canaries in the alignment gaps between its three row spans
+    (exact fp32 rows, INT4-range rows, INT8 rows, each [B, H, 128, d]).
+    .check_guards() verifies them; rows past N inside a span are unspecified."""
+    import ctypes
+    import torch
+    from quantized_attention_sage_amd import api, _lib as L
+
+    class GuardedProbeScratch(api.ProbeScratch):
+        def __init__(self):
+            n = ctypes.c_size_t()
+            L.check(L.lib().sage_probe_scratch_bytes(ctypes.byref(shape), ctypes.byref(n)))
+            self.nbytes = n.value
+            self.tensor = torch.full((self.nbytes + 2 * GUARD + 256,), CANARY, dtype=torch.uint8, device=device)
+            self._pad = (-self.tensor.data_ptr()) % 256 + GUARD
+            self.shape = (shape.B, shape.H, shape.d)
+            self.io = torch.bfloat16 if shape.dtype == L.SAGE_BF16 else torch.float16
+
+        def check_guards(self):
+            B, H, d = self.shape
+            rows = B * H * 128 * d
+            spans, off = [], 0
+            for size in (4, 2, 2):
+                spans.append((off, rows * size))
+                off = (off + rows * size + 255) // 256 * 256
+            # everything after the INT8 rows is the probe's own partial results: one span to the end
+            spans.append((off, self.nbytes - off))
+            _check_canary(self.tensor, _guard_regions(spans, self._pad, self.nbytes, self.tensor.numel()),
+                          "probe scratch")
+
+    return GuardedProbeScratch()
+
+
 def run_sage(q, k, v, dtype, causal, qk_bits=8, gran="thread", smooth=(True, True, True), p_range=448.0,
              v_range=448.0, layout="bhnd", download=BUFFERS, pv="fp8", qk_format="int"):
+    """Quantize and run attention through the C ABI on guarded buffers; checks
+    the guards and returns the buffers named in `download` and the output."""
     import torch
     from quantized_attention_sage_amd import api
     qt, kt, vt = (to_device(x, dtype, layout) for x in (q, k, v))
     params = api.make_params(qk_bits=qk_bits, gran=gran, smooth_q=smooth[0], smooth_k=smooth[1], smooth_v=smooth[2],
                              p_range=p_range, v_range=v_range, pv=pv, qk_format=qk_format)
     shape = api.make_shape(qt, kt, vt)
-    ws = api.Workspace(shape, params, qt.device)
+    ws = guarded_workspace(shape, params, qt.device)
     api.quant_qk(qt, kt, vt, params, ws, shape)
     api.quant_v(vt, params, ws, shape)
-    out = torch.empty_like(qt)
-    api.attn_fwd(ws, shape, params, causal, out)
+    g = GuardedOut(qt)
+    api.attn_fwd(ws, shape, params, causal, g.out)
     torch.cuda.synchronize()
+    ws.check_guards()
+    g.check()
     res = {name: ws.view(name).cpu().numpy() for name in download}
-    res["out"] = out.float().cpu().numpy()
+    res["out"] = g.out.float().cpu().numpy()
     return res
 
 

@@ -1,0 +1,37 @@
+"""The build's check that no scratch access (register spill or reload) sits
+inside a loop of an attention kernel, on hand-written assembly listings."""
+from quantized_attention_sage_amd.build import loops_with_scratch
+
+HEAD = "_ZN4sage12_GLOBAL__N_115attn_fwd_kernelEv:\n"
+TAIL = ".Lfunc_end0:\n"
+
+
+def test_spill_outside_the_loop_passes():
+    asm = HEAD + """\tscratch_store_dwordx2 off, v[192:193], off ; 8-byte Folded Spill
+.LBB0_2:
+\tv_add_f32_e32 v1, v2, v3
+\ts_cbranch_scc1 .LBB0_2
+\tscratch_load_dwordx2 v[192:193], off, off ; 8-byte Folded Reload
+\ts_endpgm
+""" + TAIL
+    assert loops_with_scratch(asm) == []
+
+
+def test_reload_inside_the_loop_is_found():
+    asm = HEAD + """.LBB0_2:
+\tv_add_f32_e32 v1, v2, v3
+\tscratch_load_dwordx2 v[192:193], off, off ; 8-byte Folded Reload
+\ts_branch .LBB0_2
+\ts_endpgm
+""" + TAIL
+    bad = loops_with_scratch(asm)
+    assert len(bad) == 1 and bad[0][3] == 1
+
+
+def test_forward_branch_is_not_a_loop():
+    asm = HEAD + """\ts_cbranch_execz .LBB0_4
+\tscratch_store_dword off, v7, off
+.LBB0_4:
+\ts_endpgm
+""" + TAIL
+    assert loops_with_scratch(asm) == []

@@ -20,7 +20,7 @@ from oracle import adaptive
 import oracle
 from oracle.quant import QuantParams
 from quantized_attention_sage_amd.workloads import WORKLOADS, scaled, make_inputs
-from gpu_harness import to_device, log
+from gpu_harness import to_device, log, guarded_workspace, guarded_probe_scratch, GuardedOut
 
 pytestmark = pytest.mark.gpu
 
@@ -48,12 +48,14 @@ def test_probe(case):
     qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
     params = api.make_params(qk_bits=4, gran=w.gran, qk_format=fmt4)
     shape = api.make_shape(qt, kt, vt)
-    ws = api.Workspace(shape, params, qt.device)
+    ws = guarded_workspace(shape, params, qt.device)
     if given:
         params.qk_bits = given[0]
-    scratch = api.ProbeScratch(shape, qt.device)
+    scratch = guarded_probe_scratch(shape, qt.device)
     res = api.probe_qk_bits(qt, kt, vt, params, ws, shape, causal, qb, cos_min, scratch)
     torch.cuda.synchronize()
+    ws.check_guards()
+    scratch.check_guards()
     ref, o4, o8 = (x.float().cpu().numpy() for x in scratch.rows())
     names = ("q_codes", "q_scale", "q_mean", "k_codes", "k_scale", "k_mean", "bias")
     after = {n: ws.view(n).cpu().numpy().copy() for n in names}
@@ -69,13 +71,15 @@ def test_probe(case):
     # the quantized rows equal those of the normal full-tensor call
     for bits, fmt, got in ((4, fmt4, o4), (8, "int", o8)):
         p = api.make_params(qk_bits=bits, gran=w.gran, qk_format=fmt)
-        ws2 = api.Workspace(shape, p, qt.device)
-        out = torch.empty_like(qt)
+        ws2 = guarded_workspace(shape, p, qt.device)
+        g = GuardedOut(qt)
         api.quant_qk(qt, kt, vt, p, ws2, shape)
         api.quant_v(vt, p, ws2, shape)
-        api.attn_fwd(ws2, shape, p, causal, out)
+        api.attn_fwd(ws2, shape, p, causal, g.out)
         torch.cuda.synchronize()
-        full = out.float().cpu().numpy()[:, :, rows]
+        ws2.check_guards()
+        g.check()
+        full = g.out.float().cpu().numpy()[:, :, rows]
         np.testing.assert_array_equal(got[:, :, :nr], full, err_msg=f"INT{bits} rows differ from the full call")
         if bits == res["qk_bits"]:
             # codes, scales, means and the bias (kept from the probe's first pass) as a fresh quantisation writes them
