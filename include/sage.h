@@ -14,16 +14,17 @@
  *              / _E2M3, held as E4M3 / FP6 E2M3 on the FP8 / FP6 matrix cores,
  *              with the same S)
  *   V'  = V - mean_tokens(V); V' -> FP8 E4M3 with per-channel scales
- *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles against a
- *         reference maximum m that moves only when a tile's row maximum exceeds
- *         it by more than 4 (log2 units), so P~ = 2^(s - m) <= 16 with s the
- *         score in log2 units (S sm_scale log2 e);
- *   P~  -> FP8 E4M3 with the fixed scale P_r / 16;  O = sum P~ V' / l + mean(V),
+ *   S   = dQ dK (q^ . k^) + dS;  online softmax over 128-key tiles against the
+ *         running row maximum m, so P~ = 2^(s - m) <= 1 with s the score in
+ *         log2 units (S sm_scale log2 e);
+ *   P~  -> FP8 E4M3 with the fixed scale 1 / P_r;  O = sum P~ V' / l + mean(V),
  *         l = sum of the fp32 P~.
  *
  * All entry points are plain C with device pointers, sizes and a HIP stream
  * (passed as void*, a hipStream_t; NULL is the default stream).  The library
- * never allocates or frees memory: the caller owns every buffer.  Apart from
+ * never allocates or frees memory: the caller owns every buffer (the one
+ * exception is the static workspace of sage_attn_static, a device array the
+ * library holds per GPU for callers that cannot allocate).  Apart from
  * sage_probe_qk_bits, which waits for its sums, nothing synchronises: every
  * call only enqueues work on the given stream.
  *
@@ -47,7 +48,7 @@ extern "C" {
 #define SAGE_API __attribute__((visibility("default")))
 
 /* Bumped whenever a buffer layout, a group map or a struct below changes. */
-#define SAGE_ABI_VERSION 5
+#define SAGE_ABI_VERSION 6
 
 typedef enum {
   SAGE_OK = 0,
@@ -71,7 +72,7 @@ typedef enum { SAGE_GRAN_THREAD = 0, SAGE_GRAN_WARP = 1, SAGE_GRAN_BLOCK = 2 } s
 /* Precision of the P~V product.
  *   SAGE_PV_FP8: SageAttention2 (abstract; SageAttention2++ summary 2.1): V
  *                smoothed and encoded to FP8 E4M3 per channel, P~ to FP8
- *                with the fixed scale P_r / 16, FP8 matrix cores.
+ *                with the fixed scale 1 / P_r, FP8 matrix cores.
  *   SAGE_PV_F16: the SageAttention (first version) setting the SageAttention2
  *                abstract builds on: P~ and V in the 16-bit type of the shape
  *                (round to nearest even for P~; V exactly as given, without
@@ -129,7 +130,7 @@ typedef struct {
   int32_t smooth_q;  /* 1 (default): subtract the 128-token block mean of Q   */
   int32_t smooth_k;  /* 1 (default): subtract the token mean of K             */
   int32_t smooth_v;  /* 1 (default): subtract the token mean of V             */
-  float p_range;     /* P_r in (0, 448], default 448: P~ code = E4M3(P~ * P_r / 16) */
+  float p_range;     /* P_r in (0, 448], default 448: P~ code = E4M3(P~ * P_r)    */
   float v_range;     /* V_r in (0, 448], default 448: V code = E4M3(V' V_r/amax) */
   float sm_scale;    /* softmax scale; 0 (default) means 1/sqrt(d)            */
   int32_t pv_mode;   /* sage_pv_mode, default SAGE_PV_FP8                     */
@@ -246,6 +247,25 @@ SAGE_API sage_status sage_attn_fwd(const sage_qk_buffers* qk, const sage_v_buffe
 SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, const sage_shape* s,
                                const sage_params* p, int causal, void* o, const int64_t o_stride[3],
                                void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of the library-held workspace of sage_attn_static (per GPU). */
+#define SAGE_STATIC_WORKSPACE_BYTES (64u << 20)
+
+/* sage_attn for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops and harnesses that forbid hipMalloc.
+ * Arguments as sage_attn, without the workspace: every intermediate buffer
+ * lives in a device array of SAGE_STATIC_WORKSPACE_BYTES that the library
+ * holds on each GPU it runs on until the process ends (laid out as
+ * sage_workspace_layout gives).  The caller still owns q, k, v and o.
+ * Allocates nothing (no hipMalloc, hipFree or allocating library call).
+ * Returns SAGE_EUNSUPPORTED, with nothing enqueued, when the layout's
+ * total_bytes exceeds SAGE_STATIC_WORKSPACE_BYTES, and SAGE_EINVAL when a
+ * non-NULL stream belongs to another device than the current one.  Every
+ * call on a GPU shares that GPU's array and leaves its intermediates there:
+ * calls that overlap on one GPU (other streams, other threads) race. */
+SAGE_API sage_status sage_attn_static(const void* q, const void* k, const void* v, const sage_shape* s,
+                                      const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                                      void* stream);
 
 /* Result of sage_probe_qk_bits (host memory). */
 typedef struct {

@@ -17,7 +17,8 @@ SAGE_F16, SAGE_BF16 = 0, 1
 GRAN = {"thread": 0, "warp": 1, "block": 2}
 PV_MODE = {"fp8": 0, "f16": 1}
 QK_FORMAT = {"int": 0, "mxfp4": 1, "int_e4m3": 2, "int_e2m3": 3}
-ABI_VERSION = 5
+ABI_VERSION = 6
+STATIC_WORKSPACE_BYTES = 64 << 20   # SAGE_STATIC_WORKSPACE_BYTES
 
 c_i64_3 = ctypes.c_int64 * 3
 
@@ -86,6 +87,9 @@ EXPORTS = {
     "sage_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
                                  ctypes.POINTER(Params), ctypes.c_int, ctypes.c_void_p,
                                  ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sage_attn_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
+                                        ctypes.POINTER(Params), ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]),
     "sage_probe_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]),
     "sage_probe_qk_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
                                           ctypes.POINTER(Params), ctypes.c_int, ctypes.c_int64, ctypes.c_float,

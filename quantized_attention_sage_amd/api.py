@@ -149,6 +149,23 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False
     return out
 
 
+def attn_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, out: torch.Tensor = None,
+                **kw) -> torch.Tensor:
+    """``attn`` with every intermediate in the library-held static workspace
+    (sage_attn_static): no device allocation by the library.  ``out`` is
+    allocated like ``q`` only when not given."""
+    params = make_params(**kw)
+    shape = make_shape(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out")
+    L.check(L.lib().sage_attn_static(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                     ctypes.c_void_p(v.data_ptr()), ctypes.byref(shape), ctypes.byref(params),
+                                     int(bool(causal)), ctypes.c_void_p(out.data_ptr()), _out_strides(out),
+                                     ctypes.c_void_p(_stream(q.device))))
+    return out
+
+
 class ProbeScratch:
     """Device scratch of the adaptive INT4/INT8 probe, with views of the probed rows."""
 

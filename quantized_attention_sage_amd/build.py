@@ -40,6 +40,7 @@ SOURCES = {
     "attn_pvh.hip": [],
     "attn_fp4.hip": [],
     "probe.hip": [],
+    "static_ws.hip": [],
     "sage_api.cpp": ["-x", "hip"],
 }
 

@@ -273,6 +273,32 @@ SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, cons
   return sage_attn_fwd(&qk, &vb, s, p, causal, o, o_stride, stream);
 }
 
+SAGE_API sage_status sage_attn_static(const void* q, const void* k, const void* v, const sage_shape* s,
+                                      const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                                      void* stream) {
+  sage_status st;
+  sage_layout L;
+  if ((st = sage_workspace_layout(s, p, &L))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_out(o, o_stride)))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  if (L.total_bytes > SAGE_STATIC_WORKSPACE_BYTES)
+    return fail(SAGE_EUNSUPPORTED, "the problem needs a %zu-byte workspace; the static one holds %zu bytes",
+                L.total_bytes, static_cast<size_t>(SAGE_STATIC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  int dev = -1;
+  hipError_t e = sage::static_workspace(&ws, &dev);
+  if (e != hipSuccess) return launch_result(e, "sage_attn_static (workspace address)");
+  if (stream) {
+    int sdev = -1;
+    if ((e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev)) != hipSuccess)
+      return launch_result(e, "sage_attn_static (stream device)");
+    if (sdev != dev) return fail(SAGE_EINVAL, "the stream belongs to device %d, the current device is %d", sdev, dev);
+  }
+  return sage_attn(q, k, v, s, p, causal, o, o_stride, ws, SAGE_STATIC_WORKSPACE_BYTES, stream);
+}
+
 SAGE_API sage_status sage_probe_scratch_bytes(const sage_shape* s, size_t* bytes) {
   sage_status st;
   if ((st = check_shape(s))) return st;

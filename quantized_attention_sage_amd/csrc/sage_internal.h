@@ -54,6 +54,11 @@ hipError_t launch_attn_fp4(const Problem& p, const sage_qk_buffers& qk, const sa
 hipError_t launch_attn_pvh(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
 
+// Device address of the library-held workspace of sage_attn_static
+// (SAGE_STATIC_WORKSPACE_BYTES, 256-byte aligned) on the current device, looked
+// up once per device; *device receives the current device.
+hipError_t static_workspace(void** ptr, int* device);
+
 // Heads per longest-first group of a causal grid: as many heads (a power of
 // two dividing the heads of one XCD, at most 8) as keep their streamed K/V
 // bytes within 4 MiB, one XCD's L2.

@@ -175,6 +175,28 @@ def test_entry_points_validate_before_launching():
     assert lib.sage_status_str(L.SAGE_EUNSUPPORTED) == b"unsupported"
 
 
+def test_static_entry_validates_before_launching():
+    """sage_attn_static rejects on the host, before touching any device: a
+    problem whose workspace exceeds the static array, and bad arguments."""
+    lib = L.lib()
+    p = _params()
+    fake = ctypes.c_void_p(1 << 40)
+    N, H = 8192, 16                                             # about 83 MiB of workspace
+    st = (ctypes.c_int64 * 3)(H * N * 128, N * 128, 128)
+    big = L.Shape(1, H, N, 128, L.SAGE_BF16, 0, L.c_i64_3(*st), L.c_i64_3(*st), L.c_i64_3(*st))
+    assert lib.sage_attn_static(fake, fake, fake, ctypes.byref(big), ctypes.byref(p), 0, fake, st,
+                                None) == L.SAGE_EUNSUPPORTED
+    assert b"static" in lib.sage_last_error()
+    sh = _shape()
+    strides = (ctypes.c_int64 * 3)(256000, 128000, 128)
+    assert lib.sage_attn_static(None, fake, fake, ctypes.byref(sh), ctypes.byref(p), 0, fake, strides,
+                                None) == L.SAGE_EINVAL
+    assert lib.sage_attn_static(fake, fake, fake, ctypes.byref(sh), ctypes.byref(p), 2, fake, strides,
+                                None) == L.SAGE_EINVAL                # causal must be 0/1
+    assert L.STATIC_WORKSPACE_BYTES == int(re.search(r"#define SAGE_STATIC_WORKSPACE_BYTES \((\d+)u << (\d+)\)",
+                                                     open(HEADER).read()).group(1)) << 20
+
+
 def test_probe_scratch_bytes():
     """Exact rows fp32, two outputs of the I/O type, per-split partial rows
     (at most 64 splits of whole 8-key sub-tiles, 1024 keys up to 64K keys)
