@@ -17,6 +17,9 @@ Two parts, each citing the passage of the pages it follows:
   arithmetic exactly; the attention output is float64 apart from the fp32
   values that decide an FP8 code.
 * ``metrics`` -- cosine similarity, relative L1 and RMSE ("A.2").
+* ``backward`` -- exact float64 attention gradients and the emulation of the
+  8-bit backward (the SageAttention3 abstract's 8-bit attention for forward
+  and backward propagation, read as in that module's docstring).
 * ``adaptive`` -- the adaptive INT4/INT8 choice of the SageAttention2
   abstract, read as a probe of one sampled query block per head.
 * ``fp4`` -- MXFP4 (E2M1 codes with E8M0 scales per 32 channels) for the FP4
@@ -33,7 +36,7 @@ emulation with the papers' own kernels is "parity unpinned"; what is pinned is
 agreement with exact attention when quantisation is switched off, the
 quantiser invariants, the codec, and the reduction order.
 """
-from . import fp4, fp6, fp8, reduce, quant, attention, metrics, adaptive  # noqa: F401
+from . import fp4, fp6, fp8, reduce, quant, attention, metrics, adaptive, backward  # noqa: F401
 
 from .fp8 import e4m3_decode, e4m3_encode  # noqa: F401
 from .reduce import canonical_sum, canonical_mean, pad_length  # noqa: F401
