@@ -48,7 +48,7 @@ extern "C" {
 #define SAGE_API __attribute__((visibility("default")))
 
 /* Bumped whenever a buffer layout, a group map or a struct below changes. */
-#define SAGE_ABI_VERSION 6
+#define SAGE_ABI_VERSION 7
 
 typedef enum {
   SAGE_OK = 0,
@@ -266,6 +266,67 @@ SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, cons
 SAGE_API sage_status sage_attn_static(const void* q, const void* k, const void* v, const sage_shape* s,
                                       const sage_params* p, int causal, void* o, const int64_t o_stride[3],
                                       void* stream);
+
+/* ---- 8-bit training: the forward with its row log-sum-exp, and the backward ----
+ * The SageAttention3 abstract (an 8-bit attention for forward and backward
+ * propagation; no formats on the pages).  The readings, element by element:
+ *   forward:  the method above; it also returns L_i = log2 sum_j 2^(s_ij) of
+ *             its own log2-domain scores s (K smoothed, Q-smoothing bias
+ *             added), so that P = 2^(s - L) is its softmax;
+ *   backward: FlashAttention's formulas, D_i = sum_c dO_ic O_ic,
+ *             dV = P^T dO, dP = dO V^T, dS = P o (dP - D), dQ = c dS K',
+ *             dK = c dS^T Q (c = sm_scale, K' = K - mean(K); dS K = dS K'
+ *             because each row of the exact dS sums to zero), every product
+ *             on 8-bit operands with scales constant along its reduction axis:
+ *             S from the forward's INT8 codes, scales and bias; dP in INT8
+ *             (dO one scale per token, V one per 16-key group as the THREAD
+ *             granularity's K groups; no smoothing); dV with P as E4M3 at the
+ *             fixed scale 1/P_r and dO as E4M3 per channel; dQ and dK with dS
+ *             as E4M3 under one power-of-two scale per 64-element group along
+ *             the reduced axis (per query row and 64 keys for dQ, per key and
+ *             64 queries for dK; the smallest 2^e with 448 2^e >= the group's
+ *             max |dS|), K' and Q as E4M3 per channel.  Accumulation is fp32. */
+
+/* sage_attn_fwd that also writes lse (float [B, H, N_pad], every padded row
+ * included).  qk_format SAGE_QK_INT (qk_bits 8 or 4), _INT_E4M3 or _INT_E2M3
+ * with SAGE_PV_FP8; other settings return SAGE_EUNSUPPORTED. */
+SAGE_API sage_status sage_attn_fwd_lse(const sage_qk_buffers* qk, const sage_v_buffers* vb, const sage_shape* s,
+                                       const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                                       float* lse, void* stream);
+
+/* Byte layout of the backward's intermediate buffers inside one workspace
+ * (every span 256-byte aligned):
+ *   do_codes int8 [B,H,N_pad,d], do_scale fp32 [B,H,N_pad], do_mean fp32
+ *   [B,H,N_pad/128,d] (0): INT8 dO;  v_codes int8 [B,H,N_pad,d], v_scale fp32
+ *   [B,H,N_pad/16], v_mean fp32 [B,H,d] (0), v_partial: INT8 V (the THREAD
+ *   K-side groups) and its scratch;  do8_*, q8_*, k8_* as the FP8 V buffers of
+ *   sage_v_buffers (codes uint8 [B,H,d,N_pad] in the permuted channel-major
+ *   order, scale and mean fp32 [B,H,d]; k8 holds K' = K - mean(K) and its
+ *   mean, do8 and q8 unsmoothed, means 0);  fp8_partial: their shared
+ *   scratch;  dsum fp32 [B,H,N_pad]: D (0 past N). */
+typedef struct {
+  int64_t n_pad;
+  sage_span do_codes, do_scale, do_mean, v_codes, v_scale, v_mean, v_partial;
+  sage_span do8_codes, do8_scale, do8_mean, q8_codes, q8_scale, q8_mean, k8_codes, k8_scale, k8_mean;
+  sage_span fp8_partial, dsum;
+  size_t total_bytes;
+} sage_bwd_layout;
+
+/* Host only.  Layout of the backward workspace for this problem. */
+SAGE_API sage_status sage_bwd_workspace_layout(const sage_shape* s, const sage_params* p, sage_bwd_layout* out);
+
+/* The 8-bit backward.  q, k, v: the forward's inputs (shape s); o and dout:
+ * the forward's output and its gradient, [B,H,N,d] of the shape's dtype with
+ * element strides o_stride (shared by both); lse: from sage_attn_fwd_lse; qk:
+ * the forward's sage_quant_qk buffers (same params).  Writes dq, dk, dv: fp32
+ * [B,H,N,d], contiguous, 16-byte aligned.  Supported: qk_bits 8,
+ * SAGE_GRAN_THREAD, SAGE_QK_INT, SAGE_PV_FP8 (else SAGE_EUNSUPPORTED).
+ * workspace: 256-byte aligned, ws_bytes >= sage_bwd_workspace_layout's
+ * total_bytes.  Enqueues kernels only. */
+SAGE_API sage_status sage_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const int64_t o_stride[3], const float* lse, const sage_qk_buffers* qk,
+                                   const sage_shape* s, const sage_params* p, int causal, float* dq, float* dk,
+                                   float* dv, void* workspace, size_t ws_bytes, void* stream);
 
 /* Result of sage_probe_qk_bits (host memory). */
 typedef struct {

@@ -17,7 +17,7 @@ SAGE_F16, SAGE_BF16 = 0, 1
 GRAN = {"thread": 0, "warp": 1, "block": 2}
 PV_MODE = {"fp8": 0, "f16": 1}
 QK_FORMAT = {"int": 0, "mxfp4": 1, "int_e4m3": 2, "int_e2m3": 3}
-ABI_VERSION = 6
+ABI_VERSION = 7
 STATIC_WORKSPACE_BYTES = 64 << 20   # SAGE_STATIC_WORKSPACE_BYTES
 
 c_i64_3 = ctypes.c_int64 * 3
@@ -58,6 +58,15 @@ class Layout(ctypes.Structure):
                  ("k_groups", ctypes.c_int64)] + [(n, Span) for n in SPANS] + [("total_bytes", ctypes.c_size_t)])
 
 
+BWD_SPANS = ("do_codes", "do_scale", "do_mean", "v_codes", "v_scale", "v_mean", "v_partial",
+             "do8_codes", "do8_scale", "do8_mean", "q8_codes", "q8_scale", "q8_mean", "k8_codes", "k8_scale",
+             "k8_mean", "fp8_partial", "dsum")
+
+
+class BwdLayout(ctypes.Structure):
+    _fields_ = [("n_pad", ctypes.c_int64)] + [(n, Span) for n in BWD_SPANS] + [("total_bytes", ctypes.c_size_t)]
+
+
 class ProbeResult(ctypes.Structure):
     _fields_ = [("cos_int4", ctypes.c_double), ("cos_int8", ctypes.c_double), ("rel_l1_int4", ctypes.c_double),
                 ("rel_l1_int8", ctypes.c_double), ("qk_bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
@@ -90,6 +99,16 @@ EXPORTS = {
     "sage_attn_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
                                         ctypes.POINTER(Params), ctypes.c_int, ctypes.c_void_p,
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]),
+    "sage_attn_fwd_lse": (ctypes.c_int, [ctypes.POINTER(QKBuffers), ctypes.POINTER(VBuffers), ctypes.POINTER(Shape),
+                                         ctypes.POINTER(Params), ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p, ctypes.c_void_p]),
+    "sage_bwd_workspace_layout": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(Params),
+                                                 ctypes.POINTER(BwdLayout)]),
+    "sage_attn_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p,
+                                     ctypes.POINTER(QKBuffers), ctypes.POINTER(Shape), ctypes.POINTER(Params),
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "sage_probe_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]),
     "sage_probe_qk_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shape),
                                           ctypes.POINTER(Params), ctypes.c_int, ctypes.c_int64, ctypes.c_float,

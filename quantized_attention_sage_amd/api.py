@@ -166,6 +166,71 @@ def attn_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     return out
 
 
+def attn_fwd_lse(ws: Workspace, shape: L.Shape, params: L.Params, causal: bool, out: torch.Tensor,
+                 lse: torch.Tensor):
+    """attn_fwd that also writes lse (float32 [B, H, N_pad]): log2 sum_j 2^(s_ij)."""
+    _check_tensor(out, "out")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != shape.B * shape.H * ws.layout.n_pad:
+        raise ValueError("lse must be a contiguous float32 [B, H, N_pad] tensor")
+    L.check(L.lib().sage_attn_fwd_lse(ctypes.byref(ws.qk), ctypes.byref(ws.vb), ctypes.byref(shape),
+                                      ctypes.byref(params), int(bool(causal)), ctypes.c_void_p(out.data_ptr()),
+                                      _out_strides(out), ctypes.c_void_p(lse.data_ptr()),
+                                      ctypes.c_void_p(_stream(out.device))))
+
+
+class BwdWorkspace:
+    """The backward's intermediate buffers in one device allocation, with views."""
+
+    def __init__(self, shape: L.Shape, params: L.Params, device):
+        lay = L.BwdLayout()
+        L.check(L.lib().sage_bwd_workspace_layout(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(lay)))
+        self.layout = lay
+        self.shape = (shape.B, shape.H, shape.N, shape.d)
+        self.tensor = torch.empty(lay.total_bytes + 256, dtype=torch.uint8, device=device)
+        self._pad = (-self.tensor.data_ptr()) % 256
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr() + self._pad
+
+    @property
+    def nbytes(self) -> int:
+        return self.layout.total_bytes
+
+    def view(self, name: str) -> torch.Tensor:
+        B, H, N, d = self.shape
+        n_pad = self.layout.n_pad
+        sp = getattr(self.layout, name)
+        raw = self.tensor[self._pad + sp.offset: self._pad + sp.offset + sp.bytes]
+        shapes = {
+            "do_codes": (torch.int8, (B, H, n_pad, d)), "do_scale": (torch.float32, (B, H, n_pad)),
+            "v_codes": (torch.int8, (B, H, n_pad, d)), "v_scale": (torch.float32, (B, H, n_pad // 16)),
+            "do8_codes": (torch.uint8, (B, H, d, n_pad)), "do8_scale": (torch.float32, (B, H, d)),
+            "q8_codes": (torch.uint8, (B, H, d, n_pad)), "q8_scale": (torch.float32, (B, H, d)),
+            "k8_codes": (torch.uint8, (B, H, d, n_pad)), "k8_scale": (torch.float32, (B, H, d)),
+            "k8_mean": (torch.float32, (B, H, d)), "dsum": (torch.float32, (B, H, n_pad)),
+        }
+        dt, shp = shapes[name]
+        return raw.view(dt).view(shp)
+
+
+def attn_bwd(q, k, v, o, dout, lse: torch.Tensor, ws: Workspace, shape: L.Shape, params: L.Params, causal: bool,
+             bws: BwdWorkspace, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor):
+    """The 8-bit backward: writes float32 dq, dk, dv ([B, H, N, d], contiguous)."""
+    for t_, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t_.dtype != torch.float32 or not t_.is_contiguous() or tuple(t_.shape) != tuple(q.shape):
+            raise ValueError(f"{n} must be a contiguous float32 tensor shaped like q")
+    if o.stride() != dout.stride():
+        raise ValueError("o and dout must share strides")
+    L.check(L.lib().sage_attn_bwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                                  ctypes.c_void_p(dout.data_ptr()), _out_strides(o), ctypes.c_void_p(lse.data_ptr()),
+                                  ctypes.byref(ws.qk), ctypes.byref(shape), ctypes.byref(params), int(bool(causal)),
+                                  ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()),
+                                  ctypes.c_void_p(dv.data_ptr()), ctypes.c_void_p(bws.ptr),
+                                  ctypes.c_size_t(bws.nbytes), ctypes.c_void_p(_stream(q.device))))
+
+
 class ProbeScratch:
     """Device scratch of the adaptive INT4/INT8 probe, with views of the probed rows."""
 

@@ -10,7 +10,8 @@ The attention kernels wait for their own global-to-LDS copies by count
 (s_waitcnt vmcnt).  A register spill inside their key loop would add compiler
 memory operations to those counts (which only makes the waits stricter, but
 costs a full wait for every reload), so the build reads the gfx950 assembly of
-each attention source and fails if a scratch access sits inside a loop.
+each attention source and fails if a scratch access sits inside a loop, or
+if compiler-generated code uses m0 (which the copies' inline assembly sets).
 """
 from __future__ import annotations
 
@@ -33,7 +34,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-fvisibility=
           # packed fp32 arithmetic stays off: plain v_fma/v_mul/v_add only
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # sources whose kernels must keep scratch accesses out of every loop
-LOOP_SPILL_FREE = ("attn.hip", "attn_pvh.hip", "attn_fp4.hip")
+LOOP_SPILL_FREE = ("attn.hip", "attn_pvh.hip", "attn_fp4.hip", "attn_bwd.hip")
 SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "attn.hip": [],
@@ -41,6 +42,7 @@ SOURCES = {
     "attn_fp4.hip": [],
     "probe.hip": [],
     "static_ws.hip": [],
+    "attn_bwd.hip": [],
     "sage_api.cpp": ["-x", "hip"],
 }
 
@@ -61,32 +63,78 @@ def _run(cmd, cwd=None):
 
 
 def loops_with_scratch(asm: str) -> list:
-    """(kernel, first line, last line, scratch ops) of every loop of every kernel
-    in a gfx950 assembly listing that contains a scratch access.  A loop is the
-    span from a branch target label to a later branch back to it."""
+    """(kernel, block label, first line, scratch ops) of every basic block, of
+    every kernel in a gfx950 assembly listing, that holds a scratch access and
+    lies on a cycle of the kernel's control-flow graph (can reach itself)."""
     bad = []
-    func, labels = None, {}
     lines = asm.splitlines()
-    for i, line in enumerate(lines):
-        m = re.match(r"^(_Z\S+):", line)
-        if m:
-            func, labels = m.group(1), {}
+    i = 0
+    while i < len(lines):
+        m = re.match(r"^(_Z\S+):", lines[i])
+        if not m:
+            i += 1
             continue
-        if func is None:
-            continue
-        if line.startswith(".Lfunc_end"):
-            func = None
-            continue
-        m = re.match(r"^(\.LBB\S+):", line)
-        if m:
-            labels[m.group(1)] = i
-            continue
-        m = re.match(r"^\s+s_(?:cbranch_\w+|branch)\s+(\.LBB\S+)", line)
-        if m and m.group(1) in labels:
-            lo = labels[m.group(1)]
-            n = sum(1 for j in range(lo, i) if re.match(r"^\s+scratch_", lines[j]))
-            if n:
-                bad.append((func, lo + 1, i + 1, n))
+        func, start = m.group(1), i + 1
+        end = start
+        while end < len(lines) and not lines[end].startswith(".Lfunc_end"):
+            end += 1
+        # basic blocks: one starts at the entry, at every label and after every branch
+        heads = [start]
+        for j in range(start, end):
+            if re.match(r"^\.LBB\S+:", lines[j]) and heads[-1] != j:
+                heads.append(j)
+            elif re.match(r"^\s+s_(branch|cbranch_\w+)\s", lines[j]) and j + 1 < end:
+                heads.append(j + 1)
+        heads = sorted(set(heads))
+        names = [lines[h].split(":")[0] if re.match(r"^\.LBB\S+:", lines[h]) else f"<line {h + 1}>" for h in heads]
+        index = {n: k for k, n in enumerate(names) if n.startswith(".LBB")}
+        succ, scratch = [], []
+        for k, h in enumerate(heads):
+            stop = heads[k + 1] if k + 1 < len(heads) else end
+            out, falls, n_scr = set(), True, 0
+            for j in range(h, stop):
+                ln = lines[j]
+                br = re.match(r"^\s+s_(branch|cbranch_\w+)\s+(\.LBB\S+)", ln)
+                if br:
+                    out.add(index[br.group(2)])
+                    falls = br.group(1) != "branch"
+                elif re.match(r"^\s+s_(endpgm|setpc_b64|trap)\b", ln):
+                    falls = False
+                elif re.match(r"^\s+scratch_", ln):
+                    n_scr += 1
+            if falls and k + 1 < len(heads):
+                out.add(k + 1)
+            succ.append(out)
+            scratch.append(n_scr)
+        for k, n_scr in enumerate(scratch):
+            if not n_scr:
+                continue
+            seen, todo = set(), list(succ[k])
+            while todo:
+                x = todo.pop()
+                if x in seen:
+                    continue
+                seen.add(x)
+                todo.extend(succ[x])
+            if k in seen:
+                bad.append((func, names[k], heads[k] + 1, n_scr))
+        i = end
+    return bad
+
+
+def m0_outside_inline_asm(asm: str) -> list:
+    """Line numbers where compiler-generated code names m0.  The attention
+    kernels set m0 inside their own inline assembly (global-to-LDS copies);
+    m0 is a reserved register for the compiler, so those kernels must hold no
+    compiler use of it that an inline copy could overwrite."""
+    bad, inside = [], False
+    for i, line in enumerate(asm.splitlines()):
+        if ";;#ASMSTART" in line:
+            inside = True
+        elif ";;#ASMEND" in line:
+            inside = False
+        elif not inside and re.search(r"\bm0\b", line.split(";")[0]):
+            bad.append(i + 1)
     return bad
 
 
@@ -100,9 +148,13 @@ def _compile(cc: str, tmp: str, src: str, extra: list) -> tuple:
     if temps:
         stem = os.path.splitext(src)[0]
         with open(os.path.join(wd, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s")) as fh:
-            bad = loops_with_scratch(fh.read())
+            asm = fh.read()
+        bad = loops_with_scratch(asm)
         if bad:
-            raise RuntimeError(f"{src}: scratch accesses inside a loop (kernel, lines, count): {bad}")
+            raise RuntimeError(f"{src}: scratch accesses inside a loop (kernel, block, line, count): {bad}")
+        m0 = m0_outside_inline_asm(asm)
+        if m0:
+            raise RuntimeError(f"{src}: compiler-generated uses of m0 at lines {m0[:10]}")
     return obj, out
 
 

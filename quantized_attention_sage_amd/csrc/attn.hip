@@ -57,6 +57,7 @@ struct AttnArgs {
   float scale_log2;  // sm_scale * log2(e)
   float log2_pr;     // log2(P_r)
   int lpt_g;         // causal: heads per longest-first group (map_block)
+  float* lse;        // optional: log2 sum_j 2^(s_ij) of every query row [B, H, n_pad] (nullptr: not written)
   int probe_qb;      // PROBE kernels: the one query block of every head (work-group id = head);
                      // their output row of query i is i - 128 probe_qb ([B, H, 128, d] spans)
 };
@@ -591,6 +592,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.f / ltot;
+  // l sums P~ * P_r against the running maximum m: log2 sum_j 2^(s_j) = m + log2(l) - log2(P_r).
+  if (!PROBE && a.lse != nullptr && hh == 0)
+    a.lse[static_cast<int64_t>(bh) * a.n_pad + qi] = (m + __builtin_amdgcn_logf(ltot)) - a.log2_pr;
   if (qi < a.N) {
     const int b = bh / a.H, h = bh % a.H;
     const int orow_i = PROBE ? qi - q0 : qi;
@@ -624,8 +628,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
 template <int D, bool BF16, int QKF>
 hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal, void* o,
-                     const int64_t o_stride[3], hipStream_t st, int probe_qb) {
+                     const int64_t o_stride[3], hipStream_t st, int probe_qb, float* lse) {
   AttnArgs a;
+  a.lse = lse;
   a.q_codes = qk.q_codes; a.q_scale = qk.q_scale; a.k_codes = qk.k_codes; a.k_scale = qk.k_scale;
   a.bias = qk.bias; a.v_codes = vb.v_codes; a.v_scale = vb.v_scale; a.v_mean = vb.v_mean;
   a.o = o; a.oB = o_stride[0]; a.oH = o_stride[1]; a.oN = o_stride[2];
@@ -643,23 +648,23 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
 }  // namespace
 
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
-                           void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb) {
+                           void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb, float* lse) {
   if (p.qk_held == 2) {
-    if (p.D == 128) return p.bf16 ? attn_impl<128, true, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                                  : attn_impl<128, false, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb);
-    return p.bf16 ? attn_impl<64, true, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                  : attn_impl<64, false, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+    if (p.D == 128) return p.bf16 ? attn_impl<128, true, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse)
+                                  : attn_impl<128, false, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse);
+    return p.bf16 ? attn_impl<64, true, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse)
+                  : attn_impl<64, false, 2>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse);
   }
   if (p.qk_held == 1) {
-    if (p.D == 128) return p.bf16 ? attn_impl<128, true, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                                  : attn_impl<128, false, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb);
-    return p.bf16 ? attn_impl<64, true, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                  : attn_impl<64, false, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+    if (p.D == 128) return p.bf16 ? attn_impl<128, true, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse)
+                                  : attn_impl<128, false, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse);
+    return p.bf16 ? attn_impl<64, true, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse)
+                  : attn_impl<64, false, 1>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse);
   }
-  if (p.D == 128) return p.bf16 ? attn_impl<128, true, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                                : attn_impl<128, false, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb);
-  return p.bf16 ? attn_impl<64, true, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb)
-                : attn_impl<64, false, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb);
+  if (p.D == 128) return p.bf16 ? attn_impl<128, true, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse)
+                                : attn_impl<128, false, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse);
+  return p.bf16 ? attn_impl<64, true, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse)
+                : attn_impl<64, false, 0>(p, qk, vb, causal, o, o_stride, st, probe_qb, lse);
 }
 
 }  // namespace sage

@@ -1,0 +1,471 @@
+// 8-bit attention backward for gfx950 (CDNA4).
+//
+// The SageAttention3 abstract's 8-bit attention for backward propagation,
+// read as FlashAttention's backward (D = rowsum(dO o O); P = 2^(s - L);
+// dV = P^T dO; dP = dO V^T; dS = P o (dP - D); dQ = c dS K'; dK = c dS^T Q)
+// with every product on 8-bit operands whose scales are constant along the
+// product's reduction axis (include/sage.h, sage_attn_bwd):
+//   * S and dP on v_mfma_i32_32x32x32_i8: the forward's own Q/K codes, and
+//     dO / V as INT8 with the THREAD granularity's groups;
+//   * dV, dQ and dK on v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands:
+//     P with the fixed scale 1/P_r; dS with one power-of-two (E8M0) scale per
+//     64-element group along the reduced axis, which the instruction applies
+//     per lane; dO, K' and Q with per-channel scales applied at the end.
+//
+// Two kernels, each the layout of the forward kernel with roles exchanged:
+//  * bwd_dq_kernel: one work-group of 4 waves per 128-query block; wave w
+//    owns 32 queries, lane l query l%32.  S^T = K^ Q^T and dP^T = V^ dO^T put
+//    a query's 16 keys of each 32-key subtile in one lane, so the dS group of
+//    a query row and 64 keys is that lane plus lane l^32, and the lane's FP8
+//    dS codes are its B operand of dQ^T += K'^T dS^T.
+//  * bwd_dkdv_kernel: one work-group per 128-key block; lane l holds key
+//    l%32.  S = Q^ K^T and dP = dO^ V^T put a key's 16 queries of each
+//    32-query subtile in one lane, for dV^T += dO^T P and dK^T += Q^T dS.
+// Operand tiles are staged in LDS by plain loads between two barriers per
+// tile; two work-groups per CU overlap one another's loads and products.
+#include <hip/hip_runtime.h>
+
+#include "sage_internal.h"
+
+namespace sage {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kT = 128;   // queries per block and keys per tile
+
+struct BwdArgs {
+  // forward quantisation (S recompute)
+  const int8_t* q_codes;
+  const float* q_scale;     // THREAD granularity: one per token
+  const int8_t* k_codes;
+  const float* k_scale;     // one per 16-key group
+  const float* bias;        // [B, H, nblk, n_pad], in log2 units
+  const float* lse;         // [B, H, n_pad]
+  // INT8 dO (query side) and V (key side) for dP
+  const int8_t* do_codes;
+  const float* do_scale;
+  const int8_t* v_codes;
+  const float* v_scale;
+  // E4M3 channel-major [B, H, d, n_pad] (64-token permuted groups) with per-channel scales
+  const uint8_t* do8_codes;
+  const float* do8_scale;
+  const uint8_t* q8_codes;
+  const float* q8_scale;
+  const uint8_t* k8_codes;
+  const float* k8_scale;
+  const float* dsum;        // [B, H, n_pad]
+  float* dq;
+  float* dk;
+  float* dv;                // [B, H, N, d] fp32, contiguous
+  int H, N, n_pad, nblk, causal;
+  float scale_log2;         // sm_scale * log2(e)
+  float sm_scale;
+  float p_range;
+};
+
+// 16-byte chunk swizzle inside an LDS row (bank-conflict-free fragment reads;
+// self-inverse in `chunk`).
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  constexpr int CPR = ROW_BYTES / 16;
+  constexpr int RPW = 256 / ROW_BYTES;
+  return chunk ^ ((row / RPW) & (CPR - 1));
+}
+
+// 128 rows x D bytes (row-major codes, rows r0..) into LDS at `dst`.
+template <int D>
+__device__ __forceinline__ void stage_rows(uint8_t* dst, const int8_t* src, int t) {
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < kT * CPR / 256; ++i) {
+    const int p = t + 256 * i, r = p / CPR, c = p % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r) * D + 16 * c);
+    *reinterpret_cast<uint4*>(dst + r * D + 16 * swz<D>(r, c)) = v;
+  }
+}
+
+// D channel rows x 128 tokens (channel-major codes, tokens from c0) into LDS.
+template <int D>
+__device__ __forceinline__ void stage_cm(uint8_t* dst, const uint8_t* src, int n_pad, int t) {
+#pragma unroll
+  for (int i = 0; i < D * 8 / 256; ++i) {
+    const int p = t + 256 * i, ch = p >> 3, c = p & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(ch) * n_pad + 16 * c);
+    *reinterpret_cast<uint4*>(dst + ch * kT + 16 * swz<128>(ch, c)) = v;
+  }
+}
+
+// A or B fragment of an INT8 product from a row-major tile: row 32 st + col,
+// channels 32 kk + 16 hh .. + 16.
+template <int D>
+__device__ __forceinline__ i32x4 frag_rows(const uint8_t* tile, int st, int kk, int col, int hh) {
+  const int r = 32 * st + col;
+  return *reinterpret_cast<const i32x4*>(tile + r * D + 16 * swz<D>(r, 2 * kk + hh));
+}
+
+// A fragment of an E4M3 product from a channel-major tile: channel 32 c + col,
+// tokens 64 kc + 32 hh .. + 32 (the permuted order of the stored group).
+__device__ __forceinline__ i32x8 frag_cm(const uint8_t* tile, int kc, int c, int col, int hh) {
+  const int r = 32 * c + col;
+  const i32x4 a = *reinterpret_cast<const i32x4*>(tile + r * kT + 16 * swz<128>(r, 4 * kc + 2 * hh));
+  const i32x4 b = *reinterpret_cast<const i32x4*>(tile + r * kT + 16 * swz<128>(r, 4 * kc + 2 * hh + 1));
+  i32x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
+// Smallest e with 448 2^e >= amax (amax >= 0), in [-127, 127]: from the bits
+// of amax = (1 + M/2^23) 2^E, e = E - 8 when M <= 0.75 2^23, else E - 7.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int ef = static_cast<int>((u >> 23) & 0xffu);
+  if (ef == 0) return -127;
+  const int e = (u & 0x7fffffu) <= 0x600000u ? ef - 135 : ef - 134;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E4M3 codes of 32 values a lane holds for one 64-element step (two subtiles
+// of 16), times 2^-e, packed as the 32-byte operand: word 4 sub + q4 holds
+// values 4 q4 .. 4 q4 + 3 of subtile sub.
+__device__ __forceinline__ i32x8 pack_e4m3(const float (&x)[2][16], int e) {
+  i32x8 r;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float a0 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 0], -e);
+      const float a1 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 1], -e);
+      const float a2 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 2], -e);
+      const float a3 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 3], -e);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, v, true);
+      r[4 * sub + q4] = v;
+    }
+  return r;
+}
+
+__device__ __forceinline__ float amax32(const float (&x)[2][16]) {
+  float m = 0.f;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(x[sub][r]));
+  return fmaxf(m, __shfl_xor(m, 32));
+}
+
+// dQ of one 128-query block.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int KS = D / 32, CT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kT * D + 4 * kT + 64];
+  uint8_t* tk = lds;                    // forward K codes, rows
+  uint8_t* tv = lds + kT * D;           // INT8 V, rows
+  uint8_t* tk8 = lds + 2 * kT * D;      // E4M3 K', channel-major
+  float* tb = reinterpret_cast<float*>(lds + 3 * kT * D);   // bias row of the tile
+  float* tks = tb + kT;                 // 8 K scales, then 8 V scales
+
+  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5, w = t >> 6;
+  const int bh = static_cast<int>(blockIdx.x) / a.nblk;
+  int qb = static_cast<int>(blockIdx.x) % a.nblk;
+  if (a.causal) qb = a.nblk - 1 - qb;   // longest blocks first
+  const int q0 = qb * kT, qi = q0 + 32 * w + col;
+  const int64_t row = static_cast<int64_t>(bh) * a.n_pad + qi;
+
+  i32x4 qf[KS], df[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = *reinterpret_cast<const i32x4*>(a.q_codes + row * D + 32 * s + 16 * hh);
+    df[s] = *reinterpret_cast<const i32x4*>(a.do_codes + row * D + 32 * s + 16 * hh);
+  }
+  const float dq2 = a.q_scale[row] * a.scale_log2;
+  const float sdo = a.do_scale[row];
+  const float Li = a.lse[row], Di = a.dsum[row];
+
+  f32x16 acc[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+
+  const int ntiles = a.causal ? qb + 1 : a.nblk;
+  const int8_t* kbase = a.k_codes + static_cast<int64_t>(bh) * a.n_pad * D;
+  const int8_t* vbase = a.v_codes + static_cast<int64_t>(bh) * a.n_pad * D;
+  const uint8_t* k8base = a.k8_codes + static_cast<int64_t>(bh) * D * a.n_pad;
+  const float* brow = a.bias + (static_cast<int64_t>(bh) * a.nblk + qb) * a.n_pad;
+  const float* ksc = a.k_scale + static_cast<int64_t>(bh) * (a.n_pad / 16);
+  const float* vsc = a.v_scale + static_cast<int64_t>(bh) * (a.n_pad / 16);
+
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int k0 = tt * kT;
+    __syncthreads();
+    stage_rows<D>(tk, kbase + static_cast<int64_t>(k0) * D, t);
+    stage_rows<D>(tv, vbase + static_cast<int64_t>(k0) * D, t);
+    stage_cm<D>(tk8, k8base + k0, a.n_pad, t);
+    if (t < kT) tb[t] = brow[k0 + t];
+    else if (t < kT + 8) tks[t - kT] = ksc[k0 / 16 + (t - kT)];
+    else if (t < kT + 16) tks[t - kT] = vsc[k0 / 16 + (t - kT - 8)];
+    __syncthreads();
+
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      float ds[2][16];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int st = 2 * kc + sub;
+        i32x16 S = {}, dP = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tk, st, kk, col, hh), qf[kk], S, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tv, st, kk, col, hh), df[kk], dP, 0, 0, 0);
+        }
+        const float cs = dq2 * tks[2 * st + hh];
+        const float cd = sdo * tks[8 + 2 * st + hh];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jt = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3), j = k0 + jt;
+          const bool valid = j < a.N && qi < a.N && (!a.causal || j <= qi);
+          const float s = static_cast<float>(S[r]) * cs + tb[jt];
+          const float p = valid ? __builtin_amdgcn_exp2f(s - Li) : 0.f;
+          const float tdp = static_cast<float>(dP[r]) * cd - Di;
+          ds[sub][r] = valid ? p * tdp : 0.f;
+        }
+      }
+      const int e = e8m0_exponent(amax32(ds));
+      const i32x8 db = pack_e4m3(ds, e);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm(tk8, kc, c, col, hh), db, acc[c], 0, 0, 0,
+                                                                 127, 0, e + 127);
+    }
+  }
+
+  if (qi < a.N) {
+    const float* s8 = a.k8_scale + static_cast<int64_t>(bh) * D;
+    float* out = a.dq + (static_cast<int64_t>(bh) * a.N + qi) * D;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int c0 = 32 * c + 8 * a4 + 4 * hh;
+        float4 o;
+        o.x = acc[c][4 * a4 + 0] * (a.sm_scale * s8[c0 + 0]);
+        o.y = acc[c][4 * a4 + 1] * (a.sm_scale * s8[c0 + 1]);
+        o.z = acc[c][4 * a4 + 2] * (a.sm_scale * s8[c0 + 2]);
+        o.w = acc[c][4 * a4 + 3] * (a.sm_scale * s8[c0 + 3]);
+        *reinterpret_cast<float4*>(out + c0) = o;
+      }
+  }
+}
+
+// dK and dV of one 128-key block.
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int KS = D / 32, CT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kT * D + 4 * kT * 4];
+  uint8_t* tq = lds;                    // forward Q codes, rows
+  uint8_t* tdo = lds + kT * D;          // INT8 dO, rows
+  uint8_t* tq8 = lds + 2 * kT * D;      // E4M3 Q, channel-major
+  uint8_t* tdo8 = lds + 3 * kT * D;     // E4M3 dO, channel-major
+  float* tqs = reinterpret_cast<float*>(lds + 4 * kT * D);   // Q scale * sm_scale log2 e
+  float* tds = tqs + kT;                // dO scale
+  float* tl = tds + kT;                 // L
+  float* td = tl + kT;                  // D
+
+  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5, w = t >> 6;
+  const int bh = static_cast<int>(blockIdx.x) / a.nblk;
+  const int kb = static_cast<int>(blockIdx.x) % a.nblk;   // causal: low blocks have the most queries, first
+  const int k0 = kb * kT, kj = k0 + 32 * w + col;
+  const int64_t krow = static_cast<int64_t>(bh) * a.n_pad + kj;
+
+  // The key's K and V codes (B operands) are read again at every 64-query
+  // step (L1/L2 hits): held for the whole loop they would push the kernel,
+  // with its two accumulator sets, past 256 registers.
+  const i32x4* kcode = reinterpret_cast<const i32x4*>(a.k_codes + krow * D + 16 * hh);
+  const i32x4* vcode = reinterpret_cast<const i32x4*>(a.v_codes + krow * D + 16 * hh);
+  // THREAD granularity: key j is in group 2 (j / 32) + ((j % 8) / 4)
+  const int kg = 2 * (kj >> 5) + ((kj & 7) >> 2);
+  const float dk_j = a.k_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg];
+  const float sv_j = a.v_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg];
+
+  f32x16 acck[CT], accv[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acck[c][i] = 0.f; accv[c][i] = 0.f; }
+
+  const int8_t* qbase = a.q_codes + static_cast<int64_t>(bh) * a.n_pad * D;
+  const int8_t* dobase = a.do_codes + static_cast<int64_t>(bh) * a.n_pad * D;
+  const uint8_t* q8base = a.q8_codes + static_cast<int64_t>(bh) * D * a.n_pad;
+  const uint8_t* do8base = a.do8_codes + static_cast<int64_t>(bh) * D * a.n_pad;
+  const int64_t rbase = static_cast<int64_t>(bh) * a.n_pad;
+
+  for (int qt = a.causal ? kb : 0; qt < a.nblk; ++qt) {
+    const int q0 = qt * kT;
+    const float bj = a.bias[(static_cast<int64_t>(bh) * a.nblk + qt) * a.n_pad + kj];
+    __syncthreads();
+    stage_rows<D>(tq, qbase + static_cast<int64_t>(q0) * D, t);
+    stage_rows<D>(tdo, dobase + static_cast<int64_t>(q0) * D, t);
+    stage_cm<D>(tq8, q8base + q0, a.n_pad, t);
+    stage_cm<D>(tdo8, do8base + q0, a.n_pad, t);
+    if (t < kT) {
+      tqs[t] = a.q_scale[rbase + q0 + t] * a.scale_log2;
+      tds[t] = a.do_scale[rbase + q0 + t];
+    } else {
+      tl[t - kT] = a.lse[rbase + q0 + t - kT];
+      td[t - kT] = a.dsum[rbase + q0 + t - kT];
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int kc = 0; kc < 2; ++kc) {
+      float ds[2][16];
+      i32x8 pb;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int st = 2 * kc + sub;
+        // S and P first (the K codes live only here), then dP and dS.
+        float p[16];
+        {
+          i32x16 S = {};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk)
+            S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tq, st, kk, col, hh), kcode[2 * kk], S, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int it = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3), i = q0 + it;
+            const bool valid = i < a.N && kj < a.N && (!a.causal || kj <= i);
+            const float sc = static_cast<float>(S[r]) * (tqs[it] * dk_j) + bj;
+            p[r] = valid ? __builtin_amdgcn_exp2f(sc - tl[it]) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 0] * a.p_range, p[4 * q4 + 1] * a.p_range, 0, false);
+          v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 2] * a.p_range, p[4 * q4 + 3] * a.p_range, v, true);
+          pb[4 * sub + q4] = v;
+        }
+        i32x16 dP = {};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tdo, st, kk, col, hh), vcode[2 * kk], dP, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int it = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const float tdp = static_cast<float>(dP[r]) * (tds[it] * sv_j) - td[it];
+          ds[sub][r] = p[r] * tdp;     // p is 0 wherever the entry is masked
+        }
+      }
+      const int e = e8m0_exponent(amax32(ds));
+      const i32x8 db = pack_e4m3(ds, e);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        accv[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm(tdo8, kc, c, col, hh), pb, accv[c], 0, 0, 0,
+                                                                  0, 0, 0);
+        acck[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm(tq8, kc, c, col, hh), db, acck[c], 0, 0, 0,
+                                                                  127, 0, e + 127);
+      }
+    }
+  }
+
+  if (kj < a.N) {
+    const float* sq = a.q8_scale + static_cast<int64_t>(bh) * D;
+    const float* sdo = a.do8_scale + static_cast<int64_t>(bh) * D;
+    const float inv_pr = 1.f / a.p_range;
+    float* outk = a.dk + (static_cast<int64_t>(bh) * a.N + kj) * D;
+    float* outv = a.dv + (static_cast<int64_t>(bh) * a.N + kj) * D;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int c0 = 32 * c + 8 * a4 + 4 * hh;
+        float4 ok, ov;
+        ok.x = acck[c][4 * a4 + 0] * (a.sm_scale * sq[c0 + 0]);
+        ok.y = acck[c][4 * a4 + 1] * (a.sm_scale * sq[c0 + 1]);
+        ok.z = acck[c][4 * a4 + 2] * (a.sm_scale * sq[c0 + 2]);
+        ok.w = acck[c][4 * a4 + 3] * (a.sm_scale * sq[c0 + 3]);
+        ov.x = accv[c][4 * a4 + 0] * (sdo[c0 + 0] * inv_pr);
+        ov.y = accv[c][4 * a4 + 1] * (sdo[c0 + 1] * inv_pr);
+        ov.z = accv[c][4 * a4 + 2] * (sdo[c0 + 2] * inv_pr);
+        ov.w = accv[c][4 * a4 + 3] * (sdo[c0 + 3] * inv_pr);
+        *reinterpret_cast<float4*>(outk + c0) = ok;
+        *reinterpret_cast<float4*>(outv + c0) = ov;
+      }
+  }
+}
+
+// D_i = sum_c dO_ic O_ic (fp32) of every padded row; 0 for rows >= N.  One
+// wave per row, 2 channels per lane.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(const uint16_t* o, const uint16_t* dout, int64_t sB, int64_t sH,
+                                                       int64_t sN, int H, int N, int n_pad, float* dsum) {
+  const int t = threadIdx.x, l = t & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (t >> 6);   // n_pad / 4 blocks of 4 rows
+  const int bh = static_cast<int>(blockIdx.y);
+  float acc = 0.f;
+  if (r < N) {
+    const int b = bh / H, h = bh % H;
+    const int64_t off = b * sB + h * sH + r * sN;
+    for (int c = l; c < D; c += 64) {
+      float x, y;
+      if constexpr (BF16) {
+        x = __uint_as_float(static_cast<uint32_t>(o[off + c]) << 16);
+        y = __uint_as_float(static_cast<uint32_t>(dout[off + c]) << 16);
+      } else {
+        x = static_cast<float>(__builtin_bit_cast(_Float16, o[off + c]));
+        y = static_cast<float>(__builtin_bit_cast(_Float16, dout[off + c]));
+      }
+      acc = __builtin_fmaf(x, y, acc);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  }
+  if (l == 0) dsum[static_cast<int64_t>(bh) * n_pad + r] = acc;
+}
+
+template <int D>
+hipError_t bwd_impl(const Problem& p, const BwdBuffers& bb, int causal, hipStream_t st) {
+  BwdArgs a;
+  a.q_codes = bb.qk.q_codes; a.q_scale = bb.qk.q_scale; a.k_codes = bb.qk.k_codes; a.k_scale = bb.qk.k_scale;
+  a.bias = bb.qk.bias; a.lse = bb.lse;
+  a.do_codes = bb.dov.q_codes; a.do_scale = bb.dov.q_scale; a.v_codes = bb.dov.k_codes; a.v_scale = bb.dov.k_scale;
+  a.do8_codes = bb.do8.v_codes; a.do8_scale = bb.do8.v_scale;
+  a.q8_codes = bb.q8.v_codes; a.q8_scale = bb.q8.v_scale;
+  a.k8_codes = bb.k8.v_codes; a.k8_scale = bb.k8.v_scale;
+  a.dsum = bb.dsum;
+  a.dq = bb.dq; a.dk = bb.dk; a.dv = bb.dv;
+  a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.causal = causal ? 1 : 0;
+  a.scale_log2 = p.sm_scale * 1.4426950408889634f;
+  a.sm_scale = p.sm_scale;
+  a.p_range = p.p_range;
+  const dim3 grid(p.nblk * p.B * p.H);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, float* dsum, hipStream_t st) {
+  const dim3 grid(p.n_pad / 4, p.B * p.H);
+  const uint16_t* op = static_cast<const uint16_t*>(o.ptr);
+  const uint16_t* dp = static_cast<const uint16_t*>(dout.ptr);
+  if (p.D == 128) {
+    if (p.bf16) hipLaunchKernelGGL((bwd_dsum_kernel<128, true>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
+    else hipLaunchKernelGGL((bwd_dsum_kernel<128, false>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
+  } else {
+    if (p.bf16) hipLaunchKernelGGL((bwd_dsum_kernel<64, true>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
+    else hipLaunchKernelGGL((bwd_dsum_kernel<64, false>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const Problem& p, const BwdBuffers& bb, int causal, hipStream_t st) {
+  return p.D == 128 ? bwd_impl<128>(p, bb, causal, st) : bwd_impl<64>(p, bb, causal, st);
+}
+
+}  // namespace sage

@@ -273,6 +273,140 @@ SAGE_API sage_status sage_attn(const void* q, const void* k, const void* v, cons
   return sage_attn_fwd(&qk, &vb, s, p, causal, o, o_stride, stream);
 }
 
+SAGE_API sage_status sage_attn_fwd_lse(const sage_qk_buffers* qk, const sage_v_buffers* vb, const sage_shape* s,
+                                       const sage_params* p, int causal, void* o, const int64_t o_stride[3],
+                                       float* lse, void* stream) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p)) || (st = check_qk_buffers(qk)) || (st = check_v_buffers(vb)) ||
+      (st = check_out(o, o_stride)) || (st = check_tensor(lse, "lse")))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  if (p->qk_format == SAGE_QK_MXFP4 || p->pv_mode != SAGE_PV_FP8)
+    return fail(SAGE_EUNSUPPORTED, "sage_attn_fwd_lse needs integer Q/K codes and SAGE_PV_FP8");
+  const sage::Problem pr = make_problem(s, p);
+  return launch_result(sage::launch_attn_fwd(pr, *qk, *vb, causal, o, o_stride, static_cast<hipStream_t>(stream),
+                                             -1, lse),
+                       "sage_attn_fwd_lse");
+}
+
+SAGE_API sage_status sage_bwd_workspace_layout(const sage_shape* s, const sage_params* p, sage_bwd_layout* out) {
+  sage_status st;
+  if ((st = check_shape(s)) || (st = check_params(p))) return st;
+  if (!out) return fail(SAGE_EINVAL, "layout output is NULL");
+  const int64_t BH = s->B * s->H, D = s->d;
+  const int64_t n_pad = (s->N + 127) / 128 * 128, nblk = n_pad / 128;
+  sage_bwd_layout L;
+  memset(&L, 0, sizeof(L));
+  L.n_pad = n_pad;
+  size_t off = 0;
+  auto put = [&](sage_span& sp, int64_t bytes) {
+    sp.offset = off;
+    sp.bytes = static_cast<size_t>(bytes);
+    off = round_up(off + sp.bytes, 256);
+  };
+  put(L.do_codes, BH * n_pad * D);
+  put(L.do_scale, BH * n_pad * 4);
+  put(L.do_mean, BH * nblk * D * 4);
+  put(L.v_codes, BH * n_pad * D);
+  put(L.v_scale, BH * (n_pad / 16) * 4);
+  put(L.v_mean, BH * D * 4);
+  put(L.v_partial, BH * nblk * D * 4);
+  put(L.do8_codes, BH * D * n_pad);
+  put(L.do8_scale, BH * D * 4);
+  put(L.do8_mean, BH * D * 4);
+  put(L.q8_codes, BH * D * n_pad);
+  put(L.q8_scale, BH * D * 4);
+  put(L.q8_mean, BH * D * 4);
+  put(L.k8_codes, BH * D * n_pad);
+  put(L.k8_scale, BH * D * 4);
+  put(L.k8_mean, BH * D * 4);
+  put(L.fp8_partial, BH * nblk * 3 * D * 4);
+  put(L.dsum, BH * n_pad * 4);
+  L.total_bytes = off;
+  *out = L;
+  return ok();
+}
+
+SAGE_API sage_status sage_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const int64_t o_stride[3], const float* lse, const sage_qk_buffers* qk,
+                                   const sage_shape* s, const sage_params* p, int causal, float* dq, float* dk,
+                                   float* dv, void* workspace, size_t ws_bytes, void* stream) {
+  sage_status st;
+  sage_bwd_layout L;
+  if ((st = sage_bwd_workspace_layout(s, p, &L))) return st;
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_out(o, o_stride)) || (st = check_tensor(dout, "dout")) || (st = check_tensor(lse, "lse")) ||
+      (st = check_qk_buffers(qk)) || (st = check_tensor(dq, "dq")) || (st = check_tensor(dk, "dk")) ||
+      (st = check_tensor(dv, "dv")))
+    return st;
+  if (causal != 0 && causal != 1) return fail(SAGE_EINVAL, "causal must be 0 or 1");
+  if (p->qk_bits != 8 || p->gran != SAGE_GRAN_THREAD || p->qk_format != SAGE_QK_INT || p->pv_mode != SAGE_PV_FP8)
+    return fail(SAGE_EUNSUPPORTED,
+                "sage_attn_bwd needs qk_bits 8, SAGE_GRAN_THREAD, SAGE_QK_INT and SAGE_PV_FP8");
+  if (!workspace || !aligned(workspace, 256)) return fail(SAGE_EINVAL, "workspace must be a 256-byte aligned pointer");
+  if (ws_bytes < L.total_bytes)
+    return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", ws_bytes, L.total_bytes);
+
+  const sage::Problem pr = make_problem(s, p);
+  char* base = static_cast<char*>(workspace);
+  auto at = [&](const sage_span& sp) { return base + sp.offset; };
+  sage::BwdBuffers bb;
+  bb.qk = *qk;
+  bb.lse = lse;
+  bb.dov.q_codes = reinterpret_cast<int8_t*>(at(L.do_codes));
+  bb.dov.q_scale = reinterpret_cast<float*>(at(L.do_scale));
+  bb.dov.q_mean = reinterpret_cast<float*>(at(L.do_mean));
+  bb.dov.k_codes = reinterpret_cast<int8_t*>(at(L.v_codes));
+  bb.dov.k_scale = reinterpret_cast<float*>(at(L.v_scale));
+  bb.dov.k_mean = reinterpret_cast<float*>(at(L.v_mean));
+  bb.dov.bias = nullptr;                  // not written: the INT8 dO / V pass has no bias
+  bb.dov.k_partial = reinterpret_cast<float*>(at(L.v_partial));
+  float* fp8_partial = reinterpret_cast<float*>(at(L.fp8_partial));
+  bb.do8 = {reinterpret_cast<uint8_t*>(at(L.do8_codes)), reinterpret_cast<float*>(at(L.do8_scale)),
+            reinterpret_cast<float*>(at(L.do8_mean)), fp8_partial};
+  bb.q8 = {reinterpret_cast<uint8_t*>(at(L.q8_codes)), reinterpret_cast<float*>(at(L.q8_scale)),
+           reinterpret_cast<float*>(at(L.q8_mean)), fp8_partial};
+  bb.k8 = {reinterpret_cast<uint8_t*>(at(L.k8_codes)), reinterpret_cast<float*>(at(L.k8_scale)),
+           reinterpret_cast<float*>(at(L.k8_mean)), fp8_partial};
+  bb.dsum = reinterpret_cast<float*>(at(L.dsum));
+  bb.dq = dq;
+  bb.dk = dk;
+  bb.dv = dv;
+
+  // INT8 dO (query side) and V (key side): the Q/K quantiser with the THREAD
+  // groups and no smoothing, without the bias.
+  sage::Problem pi = pr;
+  pi.smooth_q = 0;
+  pi.smooth_k = 0;
+  pi.qmax = 127;
+  pi.gran = SAGE_GRAN_THREAD;
+  pi.qk_held = 0;
+  pi.qk_mx = 0;
+  sage::QKPart no_bias;
+  no_bias.bias = false;
+  // E4M3 per channel: the V quantiser at V_r = 448, smoothing only for K.
+  sage::Problem pc = pr;
+  pc.v_range = 448.f;
+  pc.pv_f16 = 0;
+  pc.smooth_v = 0;
+  sage::Problem pk = pc;
+  pk.smooth_v = 1;
+  const sage::TensorView qv{q, s->q_stride[0], s->q_stride[1], s->q_stride[2]};
+  const sage::TensorView kv{k, s->k_stride[0], s->k_stride[1], s->k_stride[2]};
+  const sage::TensorView vv{v, s->v_stride[0], s->v_stride[1], s->v_stride[2]};
+  const sage::TensorView ov{o, o_stride[0], o_stride[1], o_stride[2]};
+  const sage::TensorView dov{dout, o_stride[0], o_stride[1], o_stride[2]};
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = sage::launch_quant_qk(pi, dov, vv, bb.dov, hs, no_bias)) != hipSuccess ||
+      (e = sage::launch_quant_v(pc, dov, bb.do8, hs)) != hipSuccess ||
+      (e = sage::launch_quant_v(pc, qv, bb.q8, hs)) != hipSuccess ||
+      (e = sage::launch_quant_v(pk, kv, bb.k8, hs)) != hipSuccess ||
+      (e = sage::launch_bwd_dsum(pr, ov, dov, bb.dsum, hs)) != hipSuccess)
+    return launch_result(e, "sage_attn_bwd (operands)");
+  return launch_result(sage::launch_attn_bwd(pr, bb, causal, hs), "sage_attn_bwd");
+}
+
 SAGE_API sage_status sage_attn_static(const void* q, const void* k, const void* v, const sage_shape* s,
                                       const sage_params* p, int causal, void* o, const int64_t o_stride[3],
                                       void* stream) {

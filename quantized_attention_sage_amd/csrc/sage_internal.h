@@ -45,14 +45,34 @@ hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const s
 hipError_t launch_quant_v(const Problem& p, TensorView v, const sage_v_buffers& out, hipStream_t st);
 // probe_qb >= 0 runs only query block probe_qb of every head (B*H work-groups)
 // and writes query 128 probe_qb + r of a head to output row r ([B, H, 128, d]).
+// lse, when not null, receives log2 sum_j 2^(s_ij) of every query row, float [B, H, n_pad].
 hipError_t launch_attn_fwd(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
-                           void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb = -1);
+                           void* o, const int64_t o_stride[3], hipStream_t st, int probe_qb = -1,
+                           float* lse = nullptr);
 // The same attention with MXFP4 Q and K codes on the scaled FP4 matrix cores (Problem::qk_mx).
 hipError_t launch_attn_fp4(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
 // The same attention with the 16-bit P~V product (Problem::pv_f16).
 hipError_t launch_attn_pvh(const Problem& p, const sage_qk_buffers& qk, const sage_v_buffers& vb, int causal,
                            void* o, const int64_t o_stride[3], hipStream_t st);
+
+// Buffers of the 8-bit backward (sage_attn_bwd).
+struct BwdBuffers {
+  sage_qk_buffers qk;     // the forward's quantisation: Q/K codes and scales, bias (S recompute)
+  const float* lse;       // the forward's log2 sum_j 2^(s_ij), [B, H, n_pad]
+  sage_qk_buffers dov;    // INT8 dO (query side) and V (key side), THREAD groups, no smoothing
+  sage_v_buffers do8;     // E4M3 dO per channel (no smoothing)
+  sage_v_buffers q8;      // E4M3 Q per channel (no smoothing)
+  sage_v_buffers k8;      // E4M3 K' = K - mean(K) per channel
+  float* dsum;            // D = rowsum(dO o O), [B, H, n_pad]
+  float* dq;
+  float* dk;
+  float* dv;              // fp32 [B, H, N, d], contiguous
+};
+// D of every padded row (0 past N); o and dout share the strides of `o`.
+hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, float* dsum, hipStream_t st);
+// dQ (one work-group per query block) and dK, dV (one per key block).
+hipError_t launch_attn_bwd(const Problem& p, const BwdBuffers& bb, int causal, hipStream_t st);
 
 // Device address of the library-held workspace of sage_attn_static
 // (SAGE_STATIC_WORKSPACE_BYTES, 256-byte aligned) on the current device, looked

@@ -137,6 +137,15 @@ def make_inputs(w: Workload):
     return rnd(q), rnd(k), rnd(v)
 
 
+def make_grad(w: Workload):
+    """The output gradient dO of a backward pass on this workload: N(0, 1)
+    per element from its own stream (PCG64(seed + 1000)), rounded once to the
+    dtype; float32 [B,H,N,d]."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + 1000))
+    g = rng.standard_normal((w.B, w.H, w.N, w.d))
+    return (round_to_bf16 if w.dtype == "bf16" else round_to_fp16)(g)
+
+
 def describe(w: Workload) -> dict:
     return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype,
             "causal": w.causal, "qk_bits": w.qk_bits, "granularity": w.gran,
