@@ -219,6 +219,63 @@ def probe_bench(args, w, qt, kt, vt, shape, ws, dev):
                       "reference_flops": ref_flops, "result": res}), flush=True)
 
 
+def backward_bench(args, w, qt, kt, vt, params, shape, ws, out, dev):
+    """One 8-bit training step: sage_quant_qk + sage_quant_v + sage_attn_fwd_lse
+    + sage_attn_bwd, timed whole and by part (HIP events on the launch stream).
+    Backward operations: the five products of the FlashAttention backward,
+    10 * B * H * N^2 * d (halved when causal); the forward's 4 * B * H * N^2 * d."""
+    import numpy as np
+    import torch
+    from quantized_attention_sage_amd import api
+    from quantized_attention_sage_amd.workloads import make_grad
+    do = torch.from_numpy(make_grad(w)).to(qt.dtype).to(dev)
+    lse = torch.empty((w.B, w.H, ws.layout.n_pad), dtype=torch.float32, device=dev)
+    bws = api.BwdWorkspace(shape, params, dev)
+    grads = [torch.empty(qt.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        api.quant_qk(qt, kt, vt, params, ws, shape)
+        api.quant_v(vt, params, ws, shape)
+        api.attn_fwd_lse(ws, shape, params, w.causal, out, lse)
+        if ev is not None:
+            ev[1].record(stream)
+        api.attn_bwd(qt, kt, vt, out, do, lse, ws, shape, params, w.causal, bws, *grads)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    bwd_ops = w.ops * 2.5
+    print(json.dumps({
+        "metric": "8-bit attention training step TOPS ((4 + 10) * B*H*N^2*d, halved if causal) of "
+                  "quant_qk + quant_v + attn_fwd_lse + attn_bwd",
+        "value": round((w.ops + bwd_ops) / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "int8 QK, dP / fp8 PV, dV, dQ, dK (" + w.dtype + " in, fp32 gradients)", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+        "breakdown_ms": {"forward": round(fwd_ms, 4), "backward": round(bwd_ms, 4)},
+        "backward_roofline": {"bound": "mfma", "achieved": round(bwd_ops / (bwd_ms * 1e-3) / 1e12, 1),
+                              "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                              "frac": round(bwd_ops / (bwd_ms * 1e-3) / 1e12 / PEAK_TOPS, 4),
+                              "ops_per_call": bwd_ops},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +291,9 @@ def main():
     ap.add_argument("--pv", choices=("fp8", "f16"), default="fp8",
                     help="P~V precision: fp8 (SageAttention2, the default) or f16 (16-bit P~ and V, "
                          "the first SageAttention's setting)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time one 8-bit training step (forward with its row log-sum-exp plus the backward) "
+                         "instead of the inference step, and print its own JSON line")
     ap.add_argument("--probe", action="store_true",
                     help="time the adaptive INT4/INT8 probe (sage_probe_qk_bits on the middle query block) "
                          "instead of the step, and print its own JSON line")
@@ -278,6 +338,13 @@ def main():
         api.attn_fwd(ws, shape, params, w.causal, out)
         if ev is not None:
             ev[3].record(stream)
+
+    if args.backward:
+        if args.qk != "int" or args.pv != "fp8" or w.qk_bits != 8 or w.gran != "thread":
+            print("--backward runs INT8 Q/K codes (THREAD groups) with FP8 P~V", file=sys.stderr)
+            sys.exit(2)
+        backward_bench(args, w, qt, kt, vt, params, shape, ws, out, dev)
+        return
 
     if args.probe:
         if args.qk == "mxfp4" or args.pv != "fp8":

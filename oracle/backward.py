@@ -141,17 +141,23 @@ def forward_with_lse(q, k, v, causal: bool, dtype: str, p: QuantParams = QuantPa
                      quantized=True):
     """The emulated training forward: O rounded to the I/O dtype (float32
     [B,H,N,d]), L (float32 [B,H,n_pad]) and the quantised buffers (qk, vq)."""
-    from .attention import emulate_attention, round_output
+    from .attention import round_output
     qk, vq = quant_qk(q, k, p), quant_v(v, p)
-    o = round_output(emulate_attention(qk, vq, causal, sm_scale, p.p_range, quantized=quantized), dtype)
     B, H, n_pad = qk["q_codes"].shape[:3]
+    N = q.shape[2]
+    o = np.full(q.shape, np.nan)
     lse = np.full((B, H, n_pad), np.nan, np.float32)
+    pscale = float(np.float32(p.p_range)) if quantized else 1.0
     for b in range(B):
         for h in range(H):
             for qb in range(n_pad // QBLOCK):
-                lse[b, h, qb * QBLOCK:(qb + 1) * QBLOCK] = lse_block(qk, vq, b, h, qb, causal, sm_scale, p.p_range,
-                                                                     quantized)
-    return o, lse, qk, vq
+                tr = []
+                ob_, rows = emulate_block(qk, vq, b, h, qb, causal, sm_scale, p.p_range, quantized=quantized,
+                                          trace=tr)
+                o[b, h, rows] = ob_
+                with np.errstate(divide="ignore"):
+                    lse[b, h, qb * QBLOCK:(qb + 1) * QBLOCK] = (tr[-1]["m"] + np.log2(tr[-1]["l"] / pscale))
+    return round_output(o[:, :, :N], dtype), lse, qk, vq
 
 
 def prepare(q, k, v, do, o, lse, qk: dict, causal: bool, sm_scale=None, p_range: float = 448.0, codecs=None):

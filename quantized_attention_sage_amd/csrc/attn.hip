@@ -223,7 +223,9 @@ __device__ __forceinline__ i32x8 cat6(i32x4 a, i32x2 b) {
 // result equals the integer product exactly and the int->float conversion
 // disappears.
 // PROBE: one work-group per head, on query block a.probe_qb only.
-template <int D, bool BF16, int QKF, bool PROBE>
+// LSE: also write log2 sum_j 2^(s_ij) of every query row to a.lse (a separate
+// instantiation, so that the inference kernel's code is untouched).
+template <int D, bool BF16, int QKF, bool PROBE, bool LSE = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int KS = D / 32;          // 32-channel fragments of Q^ and K^ per row
   constexpr bool F8QK = QKF != 0;          // a float-format QK product (E4M3 or E2M3)
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.f / ltot;
   // l sums P~ * P_r against the running maximum m: log2 sum_j 2^(s_j) = m + log2(l) - log2(P_r).
-  if (!PROBE && a.lse != nullptr && hh == 0)
+  if (LSE && hh == 0)
     a.lse[static_cast<int64_t>(bh) * a.n_pad + qi] = (m + __builtin_amdgcn_logf(ltot)) - a.log2_pr;
   if (qi < a.N) {
     const int b = bh / a.H, h = bh % a.H;
@@ -641,6 +643,7 @@ hipError_t attn_impl(const Problem& p, const sage_qk_buffers& qk, const sage_v_b
   a.probe_qb = probe_qb;
   const int grid = probe_qb >= 0 ? p.B * p.H : p.nblk * p.B * p.H;
   if (probe_qb >= 0) hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, QKF, true>), dim3(grid), dim3(256), 0, st, a);
+  else if (lse) hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, QKF, false, true>), dim3(grid), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, QKF, false>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
