@@ -10,7 +10,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libsage.so")
+# SAGE_LIBRARY names another build of the same ABI (the host-sanitizer test
+# loads one); by default the in-tree libsage.so.
+LIB_PATH = os.environ.get("SAGE_LIBRARY") or os.path.join(PKG, "libsage.so")
 
 SAGE_OK, SAGE_EINVAL, SAGE_EUNSUPPORTED, SAGE_EHIP = 0, 1, 2, 3
 SAGE_F16, SAGE_BF16 = 0, 1

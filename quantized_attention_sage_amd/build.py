@@ -44,6 +44,7 @@ SOURCES = {
     "static_ws.hip": [],
     "attn_bwd.hip": [],
     "sage_api.cpp": ["-x", "hip"],
+    "layout.cpp": ["-x", "hip"],
 }
 
 

@@ -26,8 +26,8 @@
 namespace sage {
 namespace {
 
-constexpr int kRows = 128;   // one query block
-constexpr int kSub = 8;      // split lengths past 64 Ki keys are multiples of this
+constexpr int kRows = kProbeRows;   // one query block
+constexpr int kSub = kProbeSub;     // split lengths past 64 Ki keys are multiples of this
 
 template <bool BF16>
 __device__ __forceinline__ float ld16(const void* base, int64_t i) {
@@ -277,27 +277,7 @@ __global__ void probe_total_kernel(const double* part, double* out, int BH) {
   }
 }
 
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 }  // namespace
-
-ProbeLayout probe_layout(int B, int H, int N, int D, int io_bytes) {
-  ProbeLayout L;
-  const int64_t BH = static_cast<int64_t>(B) * H;
-  const int n_pad = (N + 127) / 128 * 128;
-  // at most 64 key splits (a split's last sub-tile may be partly past its end, masked)
-  L.chunk = n_pad <= 64 * 1024 ? 1024 : ((n_pad + 63) / 64 + kSub - 1) / kSub * kSub;
-  L.splits = (n_pad + L.chunk - 1) / L.chunk;
-  size_t off = 0;
-  L.ref = off;  off = align256(off + BH * kRows * D * 4);
-  L.o4 = off;   off = align256(off + BH * kRows * D * io_bytes);
-  L.o8 = off;   off = align256(off + BH * kRows * D * io_bytes);
-  L.part = off; off = align256(off + static_cast<size_t>(L.splits) * BH * kRows * (D + 2) * 4);
-  L.sums = off; off = align256(off + BH * 8 * 8);
-  L.total = off; off = align256(off + 8 * 8);
-  L.bytes = off;
-  return L;
-}
 
 hipError_t launch_probe_reference(const Problem& p, TensorView q, TensorView k, TensorView v, int causal, int q_block,
                                   char* scratch, hipStream_t st) {

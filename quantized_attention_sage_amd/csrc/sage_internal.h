@@ -90,6 +90,9 @@ inline int lpt_group(int heads, int64_t head_bytes) {
   return g;
 }
 
+constexpr int kProbeRows = 128;   // rows of the probed query block
+constexpr int kProbeSub = 8;      // split lengths of the probe's exact reference past 64 Ki keys are multiples of this
+
 // Scratch of the adaptive INT4/INT8 probe (byte offsets, 256-byte aligned).
 struct ProbeLayout {
   size_t ref, o4, o8, part, sums, total, bytes;
