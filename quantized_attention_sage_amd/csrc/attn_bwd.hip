@@ -21,8 +21,12 @@
 //  * bwd_dkdv_kernel: one work-group per 128-key block; lane l holds key
 //    l%32.  S = Q^ K^T and dP = dO^ V^T put a key's 16 queries of each
 //    32-query subtile in one lane, for dV^T += dO^T P and dK^T += Q^T dS.
-// Operand tiles are staged in LDS by plain loads between two barriers per
-// tile; two work-groups per CU overlap one another's loads and products.
+// The dQ kernel stages its operand tiles in LDS by plain loads between two
+// barriers per tile (two work-groups per CU overlap one another's loads and
+// products).  The dK/dV kernel runs one work-group per CU (its two
+// accumulator sets fill the matrix-core registers) and copies the next query
+// tile straight into the other half of a two-slot LDS ring during the
+// current tile's products.
 #include <hip/hip_runtime.h>
 
 #include "sage_internal.h"
@@ -97,6 +101,58 @@ __device__ __forceinline__ void stage_cm(uint8_t* dst, const uint8_t* src, int n
     const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(ch) * n_pad + 16 * c);
     *reinterpret_cast<uint4*>(dst + ch * kT + 16 * swz<128>(ch, c)) = v;
   }
+}
+
+// Global -> LDS copies without registers (buffer_load ... lds: lane L's 16
+// bytes land at M0 + 16 L).  Written as inline assembly so that the compiler
+// does not track these LDS writes; every copy is waited for by count 0 before
+// the barrier that publishes it.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+
+// Per-lane source offsets of the 16-byte chunks a lane copies: chunk
+// 256 j + t of a tile (t = thread) sits at LDS chunk 256 j + t and holds
+// (row-major tile) row r, chunk swz(r, c) of the source, or (channel-major
+// tile) channel ch, chunk swz(ch, c).  The swizzle term does not depend on j,
+// which moves only the scalar offset: 4096 j bytes of rows, 32 j channels.
+template <int D>
+__device__ __forceinline__ uint32_t rows_off(int t) {
+  constexpr int CPR = D / 16;
+  const int r = t / CPR, pc = t % CPR;
+  return static_cast<uint32_t>(r * D + 16 * swz<D>(r, pc));
+}
+__device__ __forceinline__ uint32_t cm_off(int t, int n_pad) {
+  const int ch = t >> 3, vc = t & 7;
+  return static_cast<uint32_t>(ch * n_pad + 16 * swz<128>(ch, vc));
+}
+
+// Copies of a 128-row tile starting at row r0 (D / 32 per wave) and of a
+// channel-major tile starting at token c0 into the LDS tile at `lds`.
+template <int D>
+__device__ __forceinline__ void copy_rows(uint32_t lds, i32x4 rs, uint32_t voff, int r0, int w) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    dma16(rs, voff, static_cast<uint32_t>(r0 * D + 4096 * j), lds + (4 * j + w) * 1024);
+}
+template <int D>
+__device__ __forceinline__ void copy_cm(uint32_t lds, i32x4 rs, uint32_t voff, int c0, int n_pad, int w) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    dma16(rs, voff, static_cast<uint32_t>(c0) + 32u * j * static_cast<uint32_t>(n_pad), lds + (4 * j + w) * 1024);
 }
 
 // A or B fragment of an INT8 product from a row-major tile: row 32 st + col,
@@ -262,29 +318,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// dK and dV of one 128-key block.
+// dK and dV of one 128-key block.  One work-group per CU (the two
+// accumulator sets live in the matrix-core registers); the operand tiles of
+// query tile qt + 1 are copied into the second half of a two-slot LDS ring
+// while tile qt's products run.
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 32, CT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kT * D + 4 * kT * 4];
-  uint8_t* tq = lds;                    // forward Q codes, rows
-  uint8_t* tdo = lds + kT * D;          // INT8 dO, rows
-  uint8_t* tq8 = lds + 2 * kT * D;      // E4M3 Q, channel-major
-  uint8_t* tdo8 = lds + 3 * kT * D;     // E4M3 dO, channel-major
-  float* tqs = reinterpret_cast<float*>(lds + 4 * kT * D);   // Q scale * sm_scale log2 e
-  float* tds = tqs + kT;                // dO scale
-  float* tl = tds + kT;                 // L
-  float* td = tl + kT;                  // D
+  constexpr int SLOT = 4 * kT * D + 4 * kT * 4;     // Q, dO (rows), Q8, dO8 (channel-major), 4 x 128 floats
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
 
-  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5, w = t >> 6;
+  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int bh = static_cast<int>(blockIdx.x) / a.nblk;
   const int kb = static_cast<int>(blockIdx.x) % a.nblk;   // causal: low blocks have the most queries, first
   const int k0 = kb * kT, kj = k0 + 32 * w + col;
   const int64_t krow = static_cast<int64_t>(bh) * a.n_pad + kj;
 
   // The key's K and V codes (B operands) are read again at every 64-query
-  // step (L1/L2 hits): held for the whole loop they would push the kernel,
-  // with its two accumulator sets, past 256 registers.
+  // step (L1/L2 hits) rather than held across the loop.
   const i32x4* kcode = reinterpret_cast<const i32x4*>(a.k_codes + krow * D + 16 * hh);
   const i32x4* vcode = reinterpret_cast<const i32x4*>(a.v_codes + krow * D + 16 * hh);
   // THREAD granularity: key j is in group 2 (j / 32) + ((j % 8) / 4)
@@ -298,28 +351,69 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acck[c][i] = 0.f; accv[c][i] = 0.f; }
 
-  const int8_t* qbase = a.q_codes + static_cast<int64_t>(bh) * a.n_pad * D;
-  const int8_t* dobase = a.do_codes + static_cast<int64_t>(bh) * a.n_pad * D;
-  const uint8_t* q8base = a.q8_codes + static_cast<int64_t>(bh) * D * a.n_pad;
-  const uint8_t* do8base = a.do8_codes + static_cast<int64_t>(bh) * D * a.n_pad;
+  const uint32_t head_rows = static_cast<uint32_t>(a.n_pad * D);
+  const i32x4 rq = buffer_rsrc(a.q_codes + static_cast<int64_t>(bh) * a.n_pad * D, head_rows);
+  const i32x4 rdo = buffer_rsrc(a.do_codes + static_cast<int64_t>(bh) * a.n_pad * D, head_rows);
+  const i32x4 rq8 = buffer_rsrc(a.q8_codes + static_cast<int64_t>(bh) * D * a.n_pad, head_rows);
+  const i32x4 rdo8 = buffer_rsrc(a.do8_codes + static_cast<int64_t>(bh) * D * a.n_pad, head_rows);
+  const uint32_t off_rows = rows_off<D>(t), off_cm = cm_off(t, a.n_pad);
   const int64_t rbase = static_cast<int64_t>(bh) * a.n_pad;
 
-  for (int qt = a.causal ? kb : 0; qt < a.nblk; ++qt) {
+  // Slot layout: Q rows, dO rows, Q8 channels, dO8 channels, then the query
+  // rows' Q scale x sm_scale log2 e, dO scale, L and D.
+  auto copies = [&](int qt, int slot) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + slot * SLOT;
+    const int q0 = qt * kT;
+    copy_rows<D>(base, rq, off_rows, q0, w);
+    copy_rows<D>(base + kT * D, rdo, off_rows, q0, w);
+    copy_cm<D>(base + 2 * kT * D, rq8, off_cm, q0, a.n_pad, w);
+    copy_cm<D>(base + 3 * kT * D, rdo8, off_cm, q0, a.n_pad, w);
+  };
+  float sa, sb;
+  auto scalars = [&](int qt) __attribute__((always_inline)) {
+    const int q0 = qt * kT;
+    if (t < kT) {
+      sa = a.q_scale[rbase + q0 + t] * a.scale_log2;
+      sb = a.do_scale[rbase + q0 + t];
+    } else {
+      sa = a.lse[rbase + q0 + t - kT];
+      sb = a.dsum[rbase + q0 + t - kT];
+    }
+  };
+  auto put_scalars = [&](int slot) __attribute__((always_inline)) {
+    float* f = reinterpret_cast<float*>(lds + slot * SLOT + 4 * kT * D);
+    if (t < kT) {
+      f[t] = sa;
+      f[kT + t] = sb;
+    } else {
+      f[2 * kT + t - kT] = sa;
+      f[3 * kT + t - kT] = sb;
+    }
+  };
+
+  const int qt0 = a.causal ? kb : 0;
+  copies(qt0, 0);
+  scalars(qt0);
+  put_scalars(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  for (int qt = qt0; qt < a.nblk; ++qt) {
+    const int cur = (qt - qt0) & 1;
+    const bool more = qt + 1 < a.nblk;
+    if (more) {
+      copies(qt + 1, cur ^ 1);
+      scalars(qt + 1);
+    }
     const int q0 = qt * kT;
     const float bj = a.bias[(static_cast<int64_t>(bh) * a.nblk + qt) * a.n_pad + kj];
-    __syncthreads();
-    stage_rows<D>(tq, qbase + static_cast<int64_t>(q0) * D, t);
-    stage_rows<D>(tdo, dobase + static_cast<int64_t>(q0) * D, t);
-    stage_cm<D>(tq8, q8base + q0, a.n_pad, t);
-    stage_cm<D>(tdo8, do8base + q0, a.n_pad, t);
-    if (t < kT) {
-      tqs[t] = a.q_scale[rbase + q0 + t] * a.scale_log2;
-      tds[t] = a.do_scale[rbase + q0 + t];
-    } else {
-      tl[t - kT] = a.lse[rbase + q0 + t - kT];
-      td[t - kT] = a.dsum[rbase + q0 + t - kT];
-    }
-    __syncthreads();
+    const uint8_t* tq = lds + cur * SLOT;
+    const uint8_t* tdo = tq + kT * D;
+    const uint8_t* tq8 = tq + 2 * kT * D;
+    const uint8_t* tdo8 = tq + 3 * kT * D;
+    const float* tqs = reinterpret_cast<const float*>(tq + 4 * kT * D);
+    const float* tds = tqs + kT;
+    const float* tl = tds + kT;
+    const float* td = tl + kT;
 
 #pragma unroll 1
     for (int kc = 0; kc < 2; ++kc) {
@@ -328,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int st = 2 * kc + sub;
-        // S and P first (the K codes live only here), then dP and dS.
+        // S and P first, then dP and dS.
         float p[16];
         {
           i32x16 S = {};
@@ -370,6 +464,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
                                                                   127, 0, e + 127);
       }
     }
+    if (more) put_scalars(cur ^ 1);
+    // the next tile's copies and scalars are in place, and every wave is done with this tile's slot
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   if (kj < a.N) {
