@@ -146,7 +146,8 @@ typedef struct {
  *   k_mean   fp32  [B, H, d]
  *   bias     fp32  [B, H, N_pad/128, N_pad]   dS[qb, j] * sm_scale * log2(e)
  *            (the bias in the exp2 domain of the softmax); 0 for j >= N
- *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums)
+ *   k_partial fp32 [B, H, N_pad/128, d]       scratch (per-block K sums; then, when
+ *            the bias is formed, the bf16 hi/lo split of each Q block mean)
  * With SAGE_QK_INT_E4M3 q_codes and k_codes hold E4M3 bytes (same layout);
  * with SAGE_QK_INT_E2M3 each d-byte row holds the packed E2M3 slots.
  * With SAGE_QK_MXFP4 the codes and scales of Q and K are instead

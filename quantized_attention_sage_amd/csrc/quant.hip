@@ -269,14 +269,16 @@ struct QKArgs {
 };
 
 // Pass 1, two work-groups per (128-token block, head): blockIdx.z = 0 writes
-// the block's K channel sums (subtrees of the K mean's tree), z = 1 the Q
-// block mean, Q codes and scales.  With k_sums = 0 every work-group is a Q one,
-// for Q blocks q_blk0 + blockIdx.x.
+// the Q block mean, Q codes and scales, z = 1 the block's K channel sums
+// (subtrees of the K mean's tree).  Work-groups start in z order, so K is the
+// input read last, the one most likely still cached when pass 2 reads it
+// again.  With k_sums = 0 every work-group is a Q one, for Q blocks q_blk0 +
+// blockIdx.x.
 template <int D, bool BF16, bool MX>
 __global__ __launch_bounds__(kThreads) void q_quant_k_sums_kernel(QKArgs a) {
   __shared__ float lds[4 * D];
   __shared__ unsigned gmax[128];
-  const bool k_part = a.k_sums && blockIdx.z == 0;
+  const bool k_part = a.k_sums && blockIdx.z == 1;
   const int blk = k_part ? static_cast<int>(blockIdx.x) : a.q_blk0 + static_cast<int>(blockIdx.x);
   const int bh = blockIdx.y;
   const int b = bh / a.H, h = bh % a.H;
@@ -377,18 +379,6 @@ __device__ __forceinline__ float segment_tree_sum(int n, int c32, int seg, F lea
   return segsum[0][c32];
 }
 
-// K mean: one work-group per (32-channel group, head); 256 threads = 32 channels x 8 segments.
-template <int D>
-__global__ __launch_bounds__(256) void k_mean_kernel(QKArgs a) {
-  __shared__ float stk[8][32][14];
-  __shared__ float segsum[8][32];
-  const int bh = blockIdx.y, c = 32 * blockIdx.x + (threadIdx.x & 31), seg = threadIdx.x >> 5;
-  const float* part = a.out.k_partial + static_cast<int64_t>(bh) * a.nblk * D + c;
-  const float sum = segment_tree_sum(a.nblk, threadIdx.x & 31, seg, [&](int i) { return part[static_cast<int64_t>(i) * D]; },
-                                     stk, segsum);
-  if (seg == 0) a.out.k_mean[static_cast<int64_t>(bh) * D + c] = a.smooth_k ? sum / static_cast<float>(a.N) : 0.f;
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -400,15 +390,48 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, u
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2));
 }
 
+// K mean: one work-group per (32-channel group, head); 256 threads = 32
+// channels x 8 segments.  When the bias follows, the work-group then stores
+// the bf16 split of the Q block means of its channels in the k_partial words
+// it has just reduced (word (qb, c) = bf16 hi | bf16 lo << 16): the bias
+// kernel reads the split from there instead of forming it once per key block.
+template <int D>
+__global__ __launch_bounds__(256) void k_mean_kernel(QKArgs a) {
+  __shared__ float stk[8][32][14];
+  __shared__ float segsum[8][32];
+  const int bh = blockIdx.y, c = 32 * blockIdx.x + (threadIdx.x & 31), seg = threadIdx.x >> 5;
+  float* part = a.out.k_partial + static_cast<int64_t>(bh) * a.nblk * D + c;
+  const float sum = segment_tree_sum(a.nblk, threadIdx.x & 31, seg, [&](int i) { return part[static_cast<int64_t>(i) * D]; },
+                                     stk, segsum);   // every leaf is read before its first barrier
+  if (seg == 0) a.out.k_mean[static_cast<int64_t>(bh) * D + c] = a.smooth_k ? sum / static_cast<float>(a.N) : 0.f;
+  if (a.with_bias) {
+    const float* qm = a.out.q_mean + static_cast<int64_t>(bh) * a.nblk * D + c;
+    for (int qb0 = seg; qb0 < a.nblk; qb0 += 64) {
+      float mu[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mu[u] = qb0 + 8 * u < a.nblk ? qm[static_cast<int64_t>(qb0 + 8 * u) * D] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        uint32_t hi, lo;
+        split_bf16x2(mu[u], 0.f, hi, lo);
+        if (qb0 + 8 * u < a.nblk)
+          reinterpret_cast<uint32_t*>(part)[static_cast<int64_t>(qb0 + 8 * u) * D] = (hi & 0xffffu) | (lo << 16);
+      }
+    }
+  }
+}
+
 // Pass 2, one work-group per (128-key block, head): K' = K - mean, K codes and
 // scales, then the bias dS[qb, j] = mu_Q(qb) . K'_j for the block's keys and
 // every Q block, on the bf16 matrix cores with a three-product hi/lo split of
 // both operands (about 16 significant bits), stored times sm_scale * log2(e).
 // Each wave keeps the split of its 32 keys in registers; the split mu_Q rows
-// go through LDS in chunks of kBiasChunk Q blocks, shared by the four waves.
-// LDS row of D bf16 values (2D bytes): 16-byte chunk c of row r lives at chunk
-// c ^ (r & (2D/16 - 1)), so the 32 rows read together by an MFMA operand load
-// spread over the banks.
+// (formed once per head by k_mean_kernel, word (qb, c) = bf16 hi | bf16 lo <<
+// 16) go through LDS in chunks of kBiasChunk Q blocks, shared by the four
+// waves.  A store instruction writes 32 consecutive keys (128 bytes) of two Q
+// blocks.  LDS row of D bf16 values (2D bytes): 16-byte chunk c of row r lives
+// at chunk c ^ (r & (2D/16 - 1)), so the 32 rows read together by an MFMA
+// operand load spread over the banks.
 constexpr int kBiasChunk = 64;
 
 template <int D>
@@ -430,23 +453,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int t = threadIdx.x, g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
   const uint16_t* kin = a.k + b * a.ksB + h * a.ksH;
   const float* kmean = a.out.k_mean + static_cast<int64_t>(bh) * D;
-  const float* qmean = a.out.q_mean + static_cast<int64_t>(bh) * a.nblk * D;
+  const uint32_t* musplit = reinterpret_cast<const uint32_t*>(a.out.k_partial) + static_cast<int64_t>(bh) * a.nblk * D;
   const int valid = min(128, a.N - row0);
   const int w = t / 64, l = t % 64, col = l & 31, hh = l >> 5;
   const int key = 32 * w + col;
 
-  // The first mu_Q chunk is fetched before the quantisation, so that its
-  // latency overlaps it.
-  float4 mq[PPT][2];
+  // The first chunk of split-mean words is fetched before the quantisation,
+  // so that its latency overlaps it.
+  uint4 mq[PPT][2];
   auto fetch_mu = [&](int qc0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int piece = t + kThreads * i;
       const int row = piece / (D / 8), c8 = piece % (D / 8);
-      mq[i][0] = mq[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      mq[i][0] = mq[i][1] = make_uint4(0u, 0u, 0u, 0u);
       if (qc0 + row < a.nblk) {
-        mq[i][0] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qc0 + row) * D + 8 * c8);
-        mq[i][1] = *reinterpret_cast<const float4*>(qmean + static_cast<int64_t>(qc0 + row) * D + 8 * c8 + 4);
+        mq[i][0] = *reinterpret_cast<const uint4*>(musplit + static_cast<int64_t>(qc0 + row) * D + 8 * c8);
+        mq[i][1] = *reinterpret_cast<const uint4*>(musplit + static_cast<int64_t>(qc0 + row) * D + 8 * c8 + 4);
       }
     }
   };
@@ -506,17 +529,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   float* bias = a.out.bias + static_cast<int64_t>(bh) * a.nblk * a.n_pad + row0 + key;
   for (int qc0 = 0; qc0 < a.nblk; qc0 += QC) {
-    // Split this chunk into LDS (the previous chunk's reads finished at the
-    // barrier ending the last iteration), then fetch the next one.
+    // Unpack this chunk's split words into the hi and lo rows in LDS (the
+    // previous chunk's reads finished at the barrier ending the last
+    // iteration), then fetch the next chunk.
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int piece = t + kThreads * i;
       const int row = piece / (D / 8), c8 = piece % (D / 8);
+      const uint32_t wd[8] = {mq[i][0].x, mq[i][0].y, mq[i][0].z, mq[i][0].w,
+                              mq[i][1].x, mq[i][1].y, mq[i][1].z, mq[i][1].w};
       uint32_t hi[4], lo[4];
-      split_bf16x2(mq[i][0].x, mq[i][0].y, hi[0], lo[0]);
-      split_bf16x2(mq[i][0].z, mq[i][0].w, hi[1], lo[1]);
-      split_bf16x2(mq[i][1].x, mq[i][1].y, hi[2], lo[2]);
-      split_bf16x2(mq[i][1].z, mq[i][1].w, hi[3], lo[3]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        hi[p] = __builtin_amdgcn_perm(wd[2 * p + 1], wd[2 * p], 0x05040100u);   // low halves of the two words
+        lo[p] = __builtin_amdgcn_perm(wd[2 * p + 1], wd[2 * p], 0x07060302u);   // high halves
+      }
       *reinterpret_cast<uint4*>(ahi + bf_off<D>(row, c8)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       *reinterpret_cast<uint4*>(alo + bf_off<D>(row, c8)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
@@ -527,20 +554,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      // A operands (the split mu_Q rows s0 + col) are read one step ahead of
+      // their three products, so that the LDS latency overlaps them.
+      bf16x8 A_hi[2], A_lo[2];
+      auto read_a = [&](int ks) __attribute__((always_inline)) {
+        const int c16 = 2 * ks + hh;
+        A_hi[ks & 1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ahi + bf_off<D>(s0 + col, c16)));
+        A_lo[ks & 1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(alo + bf_off<D>(s0 + col, c16)));
+      };
+      read_a(0);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const int c16 = 2 * ks + hh;
-        const bf16x8 A_hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ahi + bf_off<D>(s0 + col, c16)));
-        const bf16x8 A_lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(alo + bf_off<D>(s0 + col, c16)));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Bhi[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi, Blo[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_lo, Bhi[ks], acc, 0, 0, 0);
+        if (ks + 1 < D / 16) read_a(ks + 1);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's products
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi[ks & 1], Bhi[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_hi[ks & 1], Blo[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_lo[ks & 1], Bhi[ks], acc, 0, 0, 0);
       }
       // acc[i]: Q block qc0 + s0 + 8 (i / 4) + 4 hh + i % 4, this lane's key.
+      float* dst = bias + static_cast<int64_t>(qc0 + s0 + 4 * hh) * a.n_pad;
+      if (qc0 + s0 + 32 <= a.nblk) {   // uniform: all 32 Q blocks of the group exist
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qb = qc0 + s0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (qb < a.nblk) bias[static_cast<int64_t>(qb) * a.n_pad] = acc[i] * a.scale_log2;
+        for (int i = 0; i < 16; ++i) dst[static_cast<int64_t>(8 * (i >> 2) + (i & 3)) * a.n_pad] = acc[i] * a.scale_log2;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (qc0 + s0 + 8 * (i >> 2) + 4 * hh + (i & 3) < a.nblk)
+            dst[static_cast<int64_t>(8 * (i >> 2) + (i & 3)) * a.n_pad] = acc[i] * a.scale_log2;
       }
     }
     __syncthreads();   // every wave is done with this chunk's LDS rows
@@ -831,7 +871,8 @@ hipError_t quant_v_impl(const Problem& p, TensorView v, const sage_v_buffers& ou
 
 hipError_t launch_quant_qk(const Problem& p, TensorView q, TensorView k, const sage_qk_buffers& out,
                            hipStream_t st, const QKPart& part) {
-  if (part.bias && !part.k_codes) return hipErrorInvalidValue;   // the bias is written by the K-code kernel
+  // the bias is written by the K-code kernel from the Q-mean split that the K-mean kernel forms
+  if (part.bias && (!part.k_codes || !part.k_sums)) return hipErrorInvalidValue;
   if (p.D == 128)
     return p.bf16 ? quant_qk_impl<128, true>(p, q, k, out, st, part)
                   : quant_qk_impl<128, false>(p, q, k, out, st, part);
