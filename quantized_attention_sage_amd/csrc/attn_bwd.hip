@@ -256,6 +256,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const float* ksc = a.k_scale + static_cast<int64_t>(bh) * (a.n_pad / 16);
   const float* vsc = a.v_scale + static_cast<int64_t>(bh) * (a.n_pad / 16);
 
+  // entry (query qi, key j) is visible iff j <= lim_q (-1 for padded rows)
+  const int lim_q = qi < a.N ? (a.causal ? min(a.N - 1, qi) : a.N - 1) : -1;
   for (int tt = 0; tt < ntiles; ++tt) {
     const int k0 = tt * kT;
     __syncthreads();
@@ -281,14 +283,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
         const float cs = dq2 * tks[2 * st + hh];
         const float cd = sdo * tks[8 + 2 * st + hh];
+        // P = exp2(s - L), with s taken as -inf where the entry is masked (P = 0
+        // there, and so is dS: D and the dP of padded rows and keys are finite).
+        // Key k0 + jt is visible iff jt <= rel, jt = 32 st + 8 (r / 4) + 4 hh + r % 4.
+        const int rel = lim_q - k0 - 4 * hh - 32 * st;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int jt = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3), j = k0 + jt;
-          const bool valid = j < a.N && qi < a.N && (!a.causal || j <= qi);
-          const float s = static_cast<float>(S[r]) * cs + tb[jt];
-          const float p = valid ? __builtin_amdgcn_exp2f(s - Li) : 0.f;
+          const int jt = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float x = static_cast<float>(S[r]) * cs + tb[jt] - Li;
+          x = 8 * (r >> 2) + (r & 3) <= rel ? x : -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(x);
           const float tdp = static_cast<float>(dP[r]) * cd - Di;
-          ds[sub][r] = valid ? p * tdp : 0.f;
+          ds[sub][r] = p * tdp;
         }
       }
       const int e = e8m0_exponent(amax32(ds));
@@ -344,6 +350,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kg = 2 * (kj >> 5) + ((kj & 7) >> 2);
   const float dk_j = a.k_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg];
   const float sv_j = a.v_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg];
+  const bool k_ok = kj < a.N;
 
   f32x16 acck[CT], accv[CT];
 #pragma unroll
@@ -429,12 +436,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int kk = 0; kk < KS; ++kk)
             S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tq, st, kk, col, hh), kcode[2 * kk], S, 0, 0, 0);
+          // query q0 + it is visible iff lo <= it <= hi, it = 32 st + 8 (r / 4) + 4 hh + r % 4;
+          // masked entries take s = -inf, so P = 0 (and dS = 0 below)
+          const int base_it = 32 * st + 4 * hh;
+          const int lo = (a.causal ? kj - q0 : 0) - base_it, hi = (k_ok ? a.N - 1 - q0 : -1) - base_it;
+          float4 qs4[4], l4[4];
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            qs4[a4] = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
+            l4[a4] = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int it = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3), i = q0 + it;
-            const bool valid = i < a.N && kj < a.N && (!a.causal || kj <= i);
-            const float sc = static_cast<float>(S[r]) * (tqs[it] * dk_j) + bj;
-            p[r] = valid ? __builtin_amdgcn_exp2f(sc - tl[it]) : 0.f;
+            const float qs = reinterpret_cast<const float*>(&qs4[r >> 2])[r & 3];
+            const float lr = reinterpret_cast<const float*>(&l4[r >> 2])[r & 3];
+            float x = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
+            const int o = 8 * (r >> 2) + (r & 3);
+            x = ((o >= lo) & (o <= hi)) ? x : -INFINITY;
+            p[r] = __builtin_amdgcn_exp2f(x);
           }
         }
 #pragma unroll
