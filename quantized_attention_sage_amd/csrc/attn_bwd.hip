@@ -287,10 +287,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         // there, and so is dS: D and the dP of padded rows and keys are finite).
         // Key k0 + jt is visible iff jt <= rel, jt = 32 st + 8 (r / 4) + 4 hh + r % 4.
         const int rel = lim_q - k0 - 4 * hh - 32 * st;
+        float4 b4[4];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) b4[a4] = *reinterpret_cast<const float4*>(tb + 32 * st + 4 * hh + 8 * a4);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int jt = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float x = static_cast<float>(S[r]) * cs + tb[jt] - Li;
+          float x = static_cast<float>(S[r]) * cs + reinterpret_cast<const float*>(&b4[r >> 2])[r & 3] - Li;
           x = 8 * (r >> 2) + (r & 3) <= rel ? x : -INFINITY;
           const float p = __builtin_amdgcn_exp2f(x);
           const float tdp = static_cast<float>(dP[r]) * cd - Di;
@@ -412,6 +414,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       scalars(qt + 1);
     }
     const int q0 = qt * kT;
+    // every entry of the tile visible (uniform): the per-entry mask is skipped
+    const bool tile_full = q0 + kT <= a.N && k0 + kT <= a.N && (!a.causal || k0 + kT - 1 <= q0);
     const float bj = a.bias[(static_cast<int64_t>(bh) * a.nblk + qt) * a.n_pad + kj];
     const uint8_t* tq = lds + cur * SLOT;
     const uint8_t* tdo = tq + kT * D;
@@ -446,15 +450,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             qs4[a4] = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
             l4[a4] = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
           }
+          float x[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float qs = reinterpret_cast<const float*>(&qs4[r >> 2])[r & 3];
             const float lr = reinterpret_cast<const float*>(&l4[r >> 2])[r & 3];
-            float x = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
-            const int o = 8 * (r >> 2) + (r & 3);
-            x = ((o >= lo) & (o <= hi)) ? x : -INFINITY;
-            p[r] = __builtin_amdgcn_exp2f(x);
+            x[r] = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
           }
+          if (!tile_full)   // uniform
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int o = 8 * (r >> 2) + (r & 3);
+              x[r] = ((o >= lo) & (o <= hi)) ? x[r] : -INFINITY;
+            }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
         }
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -466,10 +476,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
           dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tdo, st, kk, col, hh), vcode[2 * kk], dP, 0, 0, 0);
+        float4 dsc4[4], d4[4];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          dsc4[a4] = *reinterpret_cast<const float4*>(tds + 32 * st + 4 * hh + 8 * a4);
+          d4[a4] = *reinterpret_cast<const float4*>(td + 32 * st + 4 * hh + 8 * a4);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int it = 32 * st + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const float tdp = static_cast<float>(dP[r]) * (tds[it] * sv_j) - td[it];
+          const float dsc = reinterpret_cast<const float*>(&dsc4[r >> 2])[r & 3];
+          const float dr = reinterpret_cast<const float*>(&d4[r >> 2])[r & 3];
+          const float tdp = static_cast<float>(dP[r]) * (dsc * sv_j) - dr;
           ds[sub][r] = p[r] * tdp;     // p is 0 wherever the entry is masked
         }
       }
