@@ -187,20 +187,22 @@ __device__ __forceinline__ int e8m0_exponent(float amax) {
 
 // E4M3 codes of 32 values a lane holds for one 64-element step (two subtiles
 // of 16), times 2^-e, packed as the 32-byte operand: word 4 sub + q4 holds
-// values 4 q4 .. 4 q4 + 3 of subtile sub.
+// values 4 q4 .. 4 q4 + 3 of subtile sub.  The scaled conversion divides by
+// the power of two its scale operand's exponent field encodes (its mantissa is
+// ignored), so the scale 2^e (exponent field e + 127, the E8M0 byte) applies
+// 2^-e exactly before the rounding; |x| 2^-e <= 448 by the choice of e.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ i32x8 pack_e4m3(const float (&x)[2][16], int e) {
+  const float sc = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
   i32x8 r;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float a0 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 0], -e);
-      const float a1 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 1], -e);
-      const float a2 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 2], -e);
-      const float a3 = __builtin_amdgcn_ldexpf(x[sub][4 * q4 + 3], -e);
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-      v = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, v, true);
-      r[4 * sub + q4] = v;
+      s16x2 v = {0, 0};
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, x[sub][4 * q4 + 0], x[sub][4 * q4 + 1], sc, false);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, x[sub][4 * q4 + 2], x[sub][4 * q4 + 3], sc, true);
+      r[4 * sub + q4] = __builtin_bit_cast(int, v);
     }
   return r;
 }
