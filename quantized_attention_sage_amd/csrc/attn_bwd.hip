@@ -21,9 +21,9 @@
 //  * bwd_dkdv_kernel: one work-group per 128-key block; lane l holds key
 //    l%32.  S = Q^ K^T and dP = dO^ V^T put a key's 16 queries of each
 //    32-query subtile in one lane, for dV^T += dO^T P and dK^T += Q^T dS.
-// The dQ kernel stages its operand tiles in LDS by plain loads between two
-// barriers per tile (two work-groups per CU overlap one another's loads and
-// products).  The dK/dV kernel runs one work-group per CU (its two
+// The dQ kernel walks the keys in 64-key half tiles through a three-slot LDS
+// ring filled by direct global-to-LDS copies two half tiles ahead (two
+// work-groups per CU).  The dK/dV kernel runs one work-group per CU (its two
 // accumulator sets fill the matrix-core registers) and copies the next query
 // tile straight into the other half of a two-slot LDS ring during the
 // current tile's products.
@@ -80,33 +80,10 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ ((row / RPW) & (CPR - 1));
 }
 
-// 128 rows x D bytes (row-major codes, rows r0..) into LDS at `dst`.
-template <int D>
-__device__ __forceinline__ void stage_rows(uint8_t* dst, const int8_t* src, int t) {
-  constexpr int CPR = D / 16;
-#pragma unroll
-  for (int i = 0; i < kT * CPR / 256; ++i) {
-    const int p = t + 256 * i, r = p / CPR, c = p % CPR;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r) * D + 16 * c);
-    *reinterpret_cast<uint4*>(dst + r * D + 16 * swz<D>(r, c)) = v;
-  }
-}
-
-// D channel rows x 128 tokens (channel-major codes, tokens from c0) into LDS.
-template <int D>
-__device__ __forceinline__ void stage_cm(uint8_t* dst, const uint8_t* src, int n_pad, int t) {
-#pragma unroll
-  for (int i = 0; i < D * 8 / 256; ++i) {
-    const int p = t + 256 * i, ch = p >> 3, c = p & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(ch) * n_pad + 16 * c);
-    *reinterpret_cast<uint4*>(dst + ch * kT + 16 * swz<128>(ch, c)) = v;
-  }
-}
-
 // Global -> LDS copies without registers (buffer_load ... lds: lane L's 16
 // bytes land at M0 + 16 L).  Written as inline assembly so that the compiler
-// does not track these LDS writes; every copy is waited for by count 0 before
-// the barrier that publishes it.
+// does not track these LDS writes; each kernel waits for them by hand
+// (s_waitcnt vmcnt) before the barrier that publishes them.
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
@@ -216,23 +193,94 @@ __device__ __forceinline__ float amax32(const float (&x)[2][16]) {
   return fmaxf(m, __shfl_xor(m, 32));
 }
 
-// dQ of one 128-query block.
+// Copies of a 64-key half tile: 64 rows (row-major codes, rows r0..) and D
+// channel rows of 64 keys (channel-major codes, keys c0..; 16-byte chunk c of
+// channel row r at chunk swz<64>(r, c)).  Lane t's source chunk sits at LDS
+// chunk 256 j + t; j moves only the scalar offset (32 rows, or 64 channels).
+template <int D>
+__device__ __forceinline__ void copy_rows64(uint32_t lds, i32x4 rs, uint32_t voff, int r0, int w) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j)
+    dma16(rs, voff, static_cast<uint32_t>(r0 * D + 4096 * j), lds + (4 * j + w) * 1024);
+}
+__device__ __forceinline__ uint32_t cm64_off(int t, int n_pad) {
+  const int ch = t >> 2, c = t & 3;
+  return static_cast<uint32_t>(ch * n_pad + 16 * swz<64>(ch, c));
+}
+template <int D>
+__device__ __forceinline__ void copy_cm64(uint32_t lds, i32x4 rs, uint32_t voff, int c0, int n_pad, int w) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j)
+    dma16(rs, voff, static_cast<uint32_t>(c0) + 64u * j * static_cast<uint32_t>(n_pad), lds + (4 * j + w) * 1024);
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+// A fragment of an E4M3 product from a channel-major half tile: channel
+// 32 c + col, keys 32 hh .. + 32.
+__device__ __forceinline__ i32x8 frag_cm64(const uint8_t* tile, int c, int col, int hh) {
+  const int r = 32 * c + col;
+  const i32x4 x = *reinterpret_cast<const i32x4*>(tile + r * 64 + 16 * swz<64>(r, 2 * hh));
+  const i32x4 y = *reinterpret_cast<const i32x4*>(tile + r * 64 + 16 * swz<64>(r, 2 * hh + 1));
+  i32x8 v;
+  v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  v[4] = y[0]; v[5] = y[1]; v[6] = y[2]; v[7] = y[3];
+  return v;
+}
+
+// dQ of one 128-query block.  Keys advance in 64-key half tiles through a
+// three-slot LDS ring: half tile h + 2 is copied straight from global memory
+// (buffer_load ... lds) while half tile h is used.  Each wave issues the same
+// number of copies per half tile (NC), so at the top of step h the copies of
+// h + 1 are the only ones of this wave that may still run: a wave's vector
+// memory loads return in issue order, and the loop issues no others.
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 32, CT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kT * D + 4 * kT + 64];
-  uint8_t* tk = lds;                    // forward K codes, rows
-  uint8_t* tv = lds + kT * D;           // INT8 V, rows
-  uint8_t* tk8 = lds + 2 * kT * D;      // E4M3 K', channel-major
-  float* tb = reinterpret_cast<float*>(lds + 3 * kT * D);   // bias row of the tile
-  float* tks = tb + kT;                 // 8 K scales, then 8 V scales
+  constexpr int KH = 64;                                   // keys per half tile
+  constexpr int ROWS = KH * D;                             // bytes of one row-major half tile
+  constexpr int AUX = 3 * ROWS;                            // bias (64 floats), K scales, V scales, spare
+  constexpr int SLOT = AUX + 4 * 256;
+  constexpr int NC = 3 * (D / 64) + 1;                     // copies per wave and half tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * SLOT];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
 
-  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5, w = t >> 6;
+  const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int bh = static_cast<int>(blockIdx.x) / a.nblk;
   int qb = static_cast<int>(blockIdx.x) % a.nblk;
   if (a.causal) qb = a.nblk - 1 - qb;   // longest blocks first
   const int q0 = qb * kT, qi = q0 + 32 * w + col;
   const int64_t row = static_cast<int64_t>(bh) * a.n_pad + qi;
+
+  const int nh = 2 * (a.causal ? qb + 1 : a.nblk);     // half tiles of this block
+  const uint32_t head_rows = static_cast<uint32_t>(a.n_pad * D);
+  const i32x4 rk = buffer_rsrc(a.k_codes + static_cast<int64_t>(bh) * a.n_pad * D, head_rows);
+  const i32x4 rv = buffer_rsrc(a.v_codes + static_cast<int64_t>(bh) * a.n_pad * D, head_rows);
+  const i32x4 rk8 = buffer_rsrc(a.k8_codes + static_cast<int64_t>(bh) * D * a.n_pad, head_rows);
+  const i32x4 rb = buffer_rsrc(a.bias + (static_cast<int64_t>(bh) * a.nblk + qb) * a.n_pad,
+                               static_cast<uint32_t>(a.n_pad * 4));
+  const uint32_t nsc = static_cast<uint32_t>(a.n_pad / 16 * 4);
+  const i32x4 rks = buffer_rsrc(a.k_scale + static_cast<int64_t>(bh) * (a.n_pad / 16), nsc);
+  const i32x4 rvs = buffer_rsrc(a.v_scale + static_cast<int64_t>(bh) * (a.n_pad / 16), nsc);
+  const uint32_t off_rows = rows_off<D>(t), off_cm = cm64_off(t, a.n_pad);
+  // Slot layout: K rows, V rows, K' E4M3 channel rows, then the half tile's
+  // 64 bias values, K scales (4 used) and V scales (4 used); wave 3 copies the
+  // bias again into the spare row so that every wave issues NC copies.
+  auto copies = [&](int h, int slot) __attribute__((always_inline)) {
+    const int k0 = min(h, nh - 1) * KH;        // past the end: the last half tile again (never read)
+    const uint32_t base = lds0 + slot * SLOT;
+    copy_rows64<D>(base, rk, off_rows, k0, w);
+    copy_rows64<D>(base + ROWS, rv, off_rows, k0, w);
+    copy_cm64<D>(base + 2 * ROWS, rk8, off_cm, k0, a.n_pad, w);
+    const uint32_t lane4 = 4u * static_cast<uint32_t>(l);
+    if (w == 1) dma4(rks, lane4, static_cast<uint32_t>(4 * (k0 / 16)), base + AUX + 256);
+    else if (w == 2) dma4(rvs, lane4, static_cast<uint32_t>(4 * (k0 / 16)), base + AUX + 512);
+    else dma4(rb, lane4, static_cast<uint32_t>(4 * k0), base + AUX + (w == 0 ? 0 : 768));
+  };
+  copies(0, 0);
+  copies(1, 1);
 
   i32x4 qf[KS], df[KS];
 #pragma unroll
@@ -250,65 +298,61 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
 
-  const int ntiles = a.causal ? qb + 1 : a.nblk;
-  const int8_t* kbase = a.k_codes + static_cast<int64_t>(bh) * a.n_pad * D;
-  const int8_t* vbase = a.v_codes + static_cast<int64_t>(bh) * a.n_pad * D;
-  const uint8_t* k8base = a.k8_codes + static_cast<int64_t>(bh) * D * a.n_pad;
-  const float* brow = a.bias + (static_cast<int64_t>(bh) * a.nblk + qb) * a.n_pad;
-  const float* ksc = a.k_scale + static_cast<int64_t>(bh) * (a.n_pad / 16);
-  const float* vsc = a.v_scale + static_cast<int64_t>(bh) * (a.n_pad / 16);
-
   // entry (query qi, key j) is visible iff j <= lim_q (-1 for padded rows)
   const int lim_q = qi < a.N ? (a.causal ? min(a.N - 1, qi) : a.N - 1) : -1;
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int k0 = tt * kT;
-    __syncthreads();
-    stage_rows<D>(tk, kbase + static_cast<int64_t>(k0) * D, t);
-    stage_rows<D>(tv, vbase + static_cast<int64_t>(k0) * D, t);
-    stage_cm<D>(tk8, k8base + k0, a.n_pad, t);
-    if (t < kT) tb[t] = brow[k0 + t];
-    else if (t < kT + 8) tks[t - kT] = ksc[k0 / 16 + (t - kT)];
-    else if (t < kT + 16) tks[t - kT] = vsc[k0 / 16 + (t - kT - 8)];
-    __syncthreads();
+#pragma unroll 1
+  for (int h = 0; h < nh; ++h) {
+    // This wave's copies of half tile h are complete (only the NC of h + 1
+    // may still run); after the barrier every wave's are, and every wave is
+    // done with the slot of h - 1, which the copies of h + 2 refill.
+    if constexpr (NC == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    copies(h + 2, (h + 2) % 3);
+    const uint8_t* slot = lds + (h % 3) * SLOT;
+    const uint8_t* tk = slot;
+    const uint8_t* tv = slot + ROWS;
+    const uint8_t* tk8 = slot + 2 * ROWS;
+    const float* tb = reinterpret_cast<const float*>(slot + AUX);
+    const float* tks = tb + 64;
+    const float* tvs = tb + 128;
+    const int k0 = h * KH;
 
+    float ds[2][16];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      float ds[2][16];
+    for (int sub = 0; sub < 2; ++sub) {
+      i32x16 S = {}, dP = {};
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int st = 2 * kc + sub;
-        i32x16 S = {}, dP = {};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tk, st, kk, col, hh), qf[kk], S, 0, 0, 0);
-          dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tv, st, kk, col, hh), df[kk], dP, 0, 0, 0);
-        }
-        const float cs = dq2 * tks[2 * st + hh];
-        const float cd = sdo * tks[8 + 2 * st + hh];
-        // P = exp2(s - L), with s taken as -inf where the entry is masked (P = 0
-        // there, and so is dS: D and the dP of padded rows and keys are finite).
-        // Key k0 + jt is visible iff jt <= rel, jt = 32 st + 8 (r / 4) + 4 hh + r % 4.
-        const int rel = lim_q - k0 - 4 * hh - 32 * st;
-        float4 b4[4];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) b4[a4] = *reinterpret_cast<const float4*>(tb + 32 * st + 4 * hh + 8 * a4);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = static_cast<float>(S[r]) * cs + reinterpret_cast<const float*>(&b4[r >> 2])[r & 3] - Li;
-          x = 8 * (r >> 2) + (r & 3) <= rel ? x : -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(x);
-          const float tdp = static_cast<float>(dP[r]) * cd - Di;
-          ds[sub][r] = p * tdp;
-        }
+      for (int kk = 0; kk < KS; ++kk) {
+        S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tk, sub, kk, col, hh), qf[kk], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tv, sub, kk, col, hh), df[kk], dP, 0, 0, 0);
       }
-      const int e = e8m0_exponent(amax32(ds));
-      const i32x8 db = pack_e4m3(ds, e);
+      const float cs = dq2 * tks[2 * sub + hh];
+      const float cd = sdo * tvs[2 * sub + hh];
+      // P = exp2(s - L), with s taken as -inf where the entry is masked (P = 0
+      // there, and so is dS: D and the dP of padded rows and keys are finite).
+      // Key k0 + jt is visible iff jt <= rel, jt = 32 sub + 8 (r / 4) + 4 hh + r % 4.
+      const int rel = lim_q - k0 - 4 * hh - 32 * sub;
+      float4 b4[4];
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm(tk8, kc, c, col, hh), db, acc[c], 0, 0, 0,
-                                                                 127, 0, e + 127);
+      for (int a4 = 0; a4 < 4; ++a4) b4[a4] = *reinterpret_cast<const float4*>(tb + 32 * sub + 4 * hh + 8 * a4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = static_cast<float>(S[r]) * cs + reinterpret_cast<const float*>(&b4[r >> 2])[r & 3] - Li;
+        x = 8 * (r >> 2) + (r & 3) <= rel ? x : -INFINITY;
+        const float p = __builtin_amdgcn_exp2f(x);
+        const float tdp = static_cast<float>(dP[r]) * cd - Di;
+        ds[sub][r] = p * tdp;
+      }
     }
+    const int e = e8m0_exponent(amax32(ds));
+    const i32x8 db = pack_e4m3(ds, e);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm64(tk8, c, col, hh), db, acc[c], 0, 0, 0,
+                                                               127, 0, e + 127);
   }
+  // the copies past the end write LDS: they complete before the work-group ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (qi < a.N) {
     const float* s8 = a.k8_scale + static_cast<int64_t>(bh) * D;
