@@ -12,21 +12,20 @@
 //     64-element group along the reduced axis, which the instruction applies
 //     per lane; dO, K' and Q with per-channel scales applied at the end.
 //
-// Two kernels, each the layout of the forward kernel with roles exchanged:
+// Three kernels, each the layout of the forward kernel, two with roles
+// exchanged:
 //  * bwd_dq_kernel: one work-group of 4 waves per 128-query block; wave w
 //    owns 32 queries, lane l query l%32.  S^T = K^ Q^T and dP^T = V^ dO^T put
 //    a query's 16 keys of each 32-key subtile in one lane, so the dS group of
 //    a query row and 64 keys is that lane plus lane l^32, and the lane's FP8
 //    dS codes are its B operand of dQ^T += K'^T dS^T.
-//  * bwd_dkdv_kernel: one work-group per 128-key block; lane l holds key
-//    l%32.  S = Q^ K^T and dP = dO^ V^T put a key's 16 queries of each
-//    32-query subtile in one lane, for dV^T += dO^T P and dK^T += Q^T dS.
-// The dQ kernel walks the keys in 64-key half tiles through a three-slot LDS
-// ring filled by direct global-to-LDS copies two half tiles ahead (two
-// work-groups per CU).  The dK/dV kernel runs one work-group per CU (its two
-// accumulator sets fill the matrix-core registers) and copies the next query
-// tile straight into the other half of a two-slot LDS ring during the
-// current tile's products.
+//  * bwd_dkv_kernel<D, 1> (dV) and <D, 2> (dK): one work-group per 128-key
+//    block; lane l holds key l%32.  S = Q^ K^T (and dP = dO^ V^T) put a key's
+//    16 queries of each 32-query subtile in one lane, for dV^T += dO^T P and
+//    dK^T += Q^T dS.  Split in two so that each holds one accumulator set and
+//    two work-groups fit on a CU (the dK kernel recomputes S and P).
+// Each walks the other axis in 64-row half tiles through a three-slot LDS
+// ring filled by direct global-to-LDS copies two half tiles ahead.
 #include <hip/hip_runtime.h>
 
 #include "sage_internal.h"
@@ -372,15 +371,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// dK and dV of one 128-key block.  One work-group per CU (the two
-// accumulator sets live in the matrix-core registers); the operand tiles of
-// query tile qt + 1 are copied into the second half of a two-slot LDS ring
-// while tile qt's products run.
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+// dV (PART 1) or dK (PART 2) of one 128-key block: lane l holds key l%32 of
+// its wave's 32 keys; S = Q^ K^T (and, for dK, dP = dO^ V^T) put a key's 16
+// queries of a subtile in one lane.  Queries advance in 64-query half tiles
+// through a three-slot LDS ring filled by direct copies two half tiles ahead,
+// as in the dQ kernel (NC copies per wave and half tile, waited for by count).
+// One accumulator set per kernel keeps two work-groups on a CU.
+//   dV^T += dO'^T P^ (P^ = E4M3(P P_r)): Q rows, dO' (E4M3) channel rows, Q
+//     scale and L per query.
+//   dK^T += Q'^T dS^ (dS^ = E4M3(dS 2^-e) per 64-query group): Q rows, dO
+//     rows, Q' (E4M3) channel rows, Q scale, dO scale, L and D per query.
+template <int D, int PART>
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr bool DK = PART == 2;
   constexpr int KS = D / 32, CT = D / 32;
-  constexpr int SLOT = 4 * kT * D + 4 * kT * 4;     // Q, dO (rows), Q8, dO8 (channel-major), 4 x 128 floats
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
+  constexpr int QH = 64;                                   // queries per half tile
+  constexpr int ROWS = QH * D;                             // bytes of one row-major half tile
+  constexpr int NT = DK ? 3 : 2;                           // code tiles per slot
+  constexpr int AUX = NT * ROWS;                           // 4 x 64 floats of per-query scalars
+  constexpr int SLOT = AUX + 4 * 256;
+  constexpr int NC = NT * (D / 64) + 1;                    // copies per wave and half tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * SLOT];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
 
   const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
@@ -389,190 +400,172 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kb = static_cast<int>(blockIdx.x) % a.nblk;   // causal: low blocks have the most queries, first
   const int k0 = kb * kT, kj = k0 + 32 * w + col;
   const int64_t krow = static_cast<int64_t>(bh) * a.n_pad + kj;
-
-  // The key's K and V codes (B operands) are read again at every 64-query
-  // step (L1/L2 hits) rather than held across the loop.
-  const i32x4* kcode = reinterpret_cast<const i32x4*>(a.k_codes + krow * D + 16 * hh);
-  const i32x4* vcode = reinterpret_cast<const i32x4*>(a.v_codes + krow * D + 16 * hh);
-  // THREAD granularity: key j is in group 2 (j / 32) + ((j % 8) / 4)
-  const int kg = 2 * (kj >> 5) + ((kj & 7) >> 2);
-  const float dk_j = a.k_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg];
-  const float sv_j = a.v_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg];
   const bool k_ok = kj < a.N;
 
-  f32x16 acck[CT], accv[CT];
+  // The key's K (and V) codes, B operands of S (and dP), held for the kernel.
+  i32x4 kcode[KS], vcode[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    kcode[kk] = *reinterpret_cast<const i32x4*>(a.k_codes + krow * D + 32 * kk + 16 * hh);
+    if constexpr (DK) vcode[kk] = *reinterpret_cast<const i32x4*>(a.v_codes + krow * D + 32 * kk + 16 * hh);
+  }
+  // THREAD granularity: key j is in group 2 (j / 32) + ((j % 8) / 4); the
+  // exp2-domain factor sm_scale log2 e rides on the key's scale
+  const int kg = 2 * (kj >> 5) + ((kj & 7) >> 2);
+  const float dk_j = a.k_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg] * a.scale_log2;
+  const float sv_j = DK ? a.v_scale[static_cast<int64_t>(bh) * (a.n_pad / 16) + kg] : 0.f;
+
+  f32x16 acc[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acck[c][i] = 0.f; accv[c][i] = 0.f; }
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
 
   const uint32_t head_rows = static_cast<uint32_t>(a.n_pad * D);
   const i32x4 rq = buffer_rsrc(a.q_codes + static_cast<int64_t>(bh) * a.n_pad * D, head_rows);
   const i32x4 rdo = buffer_rsrc(a.do_codes + static_cast<int64_t>(bh) * a.n_pad * D, head_rows);
-  const i32x4 rq8 = buffer_rsrc(a.q8_codes + static_cast<int64_t>(bh) * D * a.n_pad, head_rows);
-  const i32x4 rdo8 = buffer_rsrc(a.do8_codes + static_cast<int64_t>(bh) * D * a.n_pad, head_rows);
-  const uint32_t off_rows = rows_off<D>(t), off_cm = cm_off(t, a.n_pad);
+  const i32x4 r8 = buffer_rsrc((DK ? a.q8_codes : a.do8_codes) + static_cast<int64_t>(bh) * D * a.n_pad, head_rows);
+  const uint32_t head_f = static_cast<uint32_t>(a.n_pad * 4);
   const int64_t rbase = static_cast<int64_t>(bh) * a.n_pad;
+  const i32x4 rqs = buffer_rsrc(a.q_scale + rbase, head_f);
+  const i32x4 rl = buffer_rsrc(a.lse + rbase, head_f);
+  const i32x4 rds = buffer_rsrc(a.do_scale + rbase, head_f);
+  const i32x4 rd = buffer_rsrc(a.dsum + rbase, head_f);
+  const uint32_t off_rows = rows_off<D>(t), off_cm = cm64_off(t, a.n_pad);
 
-  // Slot layout: Q rows, dO rows, Q8 channels, dO8 channels, then the query
-  // rows' Q scale x sm_scale log2 e, dO scale, L and D.
-  auto copies = [&](int qt, int slot) __attribute__((always_inline)) {
+  const int h0 = a.causal ? 2 * kb : 0, nh = 2 * a.nblk;
+  // Slot layout: Q rows, [dO rows,] the E4M3 channel rows (dO' for dV, Q' for
+  // dK), then 64 floats each of Q scale, L, dO scale and D (dV: the last two
+  // rows take spare copies of Q scale so that every wave issues NC copies).
+  auto copies = [&](int h, int slot) __attribute__((always_inline)) {
+    const int q0 = min(h, nh - 1) * QH;        // past the end: the last half tile again (never read)
     const uint32_t base = lds0 + slot * SLOT;
-    const int q0 = qt * kT;
-    copy_rows<D>(base, rq, off_rows, q0, w);
-    copy_rows<D>(base + kT * D, rdo, off_rows, q0, w);
-    copy_cm<D>(base + 2 * kT * D, rq8, off_cm, q0, a.n_pad, w);
-    copy_cm<D>(base + 3 * kT * D, rdo8, off_cm, q0, a.n_pad, w);
+    copy_rows64<D>(base, rq, off_rows, q0, w);
+    if constexpr (DK) copy_rows64<D>(base + ROWS, rdo, off_rows, q0, w);
+    copy_cm64<D>(base + (NT - 1) * ROWS, r8, off_cm, q0, a.n_pad, w);
+    const uint32_t lane4 = 4u * static_cast<uint32_t>(l), so = static_cast<uint32_t>(4 * q0);
+    const uint32_t dst = base + AUX + 256 * w;
+    if (w == 0 || (!DK && w != 1)) dma4(rqs, lane4, so, dst);
+    else if (w == 1) dma4(rl, lane4, so, dst);
+    else if (w == 2) dma4(rds, lane4, so, dst);
+    else dma4(rd, lane4, so, dst);
   };
-  float sa, sb;
-  auto scalars = [&](int qt) __attribute__((always_inline)) {
-    const int q0 = qt * kT;
-    if (t < kT) {
-      sa = a.q_scale[rbase + q0 + t] * a.scale_log2;
-      sb = a.do_scale[rbase + q0 + t];
-    } else {
-      sa = a.lse[rbase + q0 + t - kT];
-      sb = a.dsum[rbase + q0 + t - kT];
-    }
-  };
-  auto put_scalars = [&](int slot) __attribute__((always_inline)) {
-    float* f = reinterpret_cast<float*>(lds + slot * SLOT + 4 * kT * D);
-    if (t < kT) {
-      f[t] = sa;
-      f[kT + t] = sb;
-    } else {
-      f[2 * kT + t - kT] = sa;
-      f[3 * kT + t - kT] = sb;
-    }
-  };
-
-  const int qt0 = a.causal ? kb : 0;
-  copies(qt0, 0);
-  scalars(qt0);
-  put_scalars(0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  for (int qt = qt0; qt < a.nblk; ++qt) {
-    const int cur = (qt - qt0) & 1;
-    const bool more = qt + 1 < a.nblk;
-    if (more) {
-      copies(qt + 1, cur ^ 1);
-      scalars(qt + 1);
-    }
-    const int q0 = qt * kT;
-    // every entry of the tile visible (uniform): the per-entry mask is skipped
-    const bool tile_full = q0 + kT <= a.N && k0 + kT <= a.N && (!a.causal || k0 + kT - 1 <= q0);
-    const float bj = a.bias[(static_cast<int64_t>(bh) * a.nblk + qt) * a.n_pad + kj];
-    const uint8_t* tq = lds + cur * SLOT;
-    const uint8_t* tdo = tq + kT * D;
-    const uint8_t* tq8 = tq + 2 * kT * D;
-    const uint8_t* tdo8 = tq + 3 * kT * D;
-    const float* tqs = reinterpret_cast<const float*>(tq + 4 * kT * D);
-    const float* tds = tqs + kT;
-    const float* tl = tds + kT;
-    const float* td = tl + kT;
+  copies(h0, 0);
+  copies(h0 + 1, 1);
 
 #pragma unroll 1
-    for (int kc = 0; kc < 2; ++kc) {
-      float ds[2][16];
-      i32x8 pb;
+  for (int h = h0; h < nh; ++h) {
+    // This wave's copies of half tile h are complete (only the NC of h + 1
+    // may still run); after the barrier every wave's are, and every wave is
+    // done with the slot of h - 1, which the copies of h + 2 refill.
+    if constexpr (NC == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (NC == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (NC == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    copies(h + 2, (h + 2 - h0) % 3);
+    const uint8_t* slot = lds + ((h - h0) % 3) * SLOT;
+    const uint8_t* tq = slot;
+    const uint8_t* tdo = slot + ROWS;
+    const uint8_t* t8 = slot + (NT - 1) * ROWS;
+    const float* tqs = reinterpret_cast<const float*>(slot + AUX);
+    const float* tl = tqs + 64;
+    const float* tds = tqs + 128;
+    const float* td = tqs + 192;
+    const int q0 = h * QH;
+    const float bj = a.bias[(static_cast<int64_t>(bh) * a.nblk + (q0 >> 7)) * a.n_pad + kj];
+    // every entry of the half tile visible (uniform): no per-entry mask
+    const bool full = q0 + QH <= a.N && k0 + kT <= a.N && (!a.causal || k0 + kT - 1 <= q0);
+
+    float ds[2][16];
+    i32x8 pb;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int st = 2 * kc + sub;
-        // S and P first, then dP and dS.
-        float p[16];
-        {
-          i32x16 S = {};
+    for (int sub = 0; sub < 2; ++sub) {
+      i32x16 S = {};
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-            S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tq, st, kk, col, hh), kcode[2 * kk], S, 0, 0, 0);
-          // query q0 + it is visible iff lo <= it <= hi, it = 32 st + 8 (r / 4) + 4 hh + r % 4;
-          // masked entries take s = -inf, so P = 0 (and dS = 0 below)
-          const int base_it = 32 * st + 4 * hh;
-          const int lo = (a.causal ? kj - q0 : 0) - base_it, hi = (k_ok ? a.N - 1 - q0 : -1) - base_it;
-          float4 qs4[4], l4[4];
+      for (int kk = 0; kk < KS; ++kk)
+        S = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tq, sub, kk, col, hh), kcode[kk], S, 0, 0, 0);
+      // query q0 + it is visible iff lo <= it <= hi, it = 32 sub + 8 (r / 4) + 4 hh + r % 4;
+      // masked entries take s = -inf, so P = 0 (and dS = 0)
+      const int base_it = 32 * sub + 4 * hh;
+      const int lo = (a.causal ? kj - q0 : 0) - base_it, hi = (k_ok ? a.N - 1 - q0 : -1) - base_it;
+      float4 qs4[4], l4[4];
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            qs4[a4] = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
-            l4[a4] = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
-          }
-          float x[16];
+      for (int a4 = 0; a4 < 4; ++a4) {
+        qs4[a4] = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
+        l4[a4] = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
+      }
+      float x[16], p[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float qs = reinterpret_cast<const float*>(&qs4[r >> 2])[r & 3];
-            const float lr = reinterpret_cast<const float*>(&l4[r >> 2])[r & 3];
-            x[r] = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
-          }
-          if (!tile_full)   // uniform
+      for (int r = 0; r < 16; ++r) {
+        const float qs = reinterpret_cast<const float*>(&qs4[r >> 2])[r & 3];
+        const float lr = reinterpret_cast<const float*>(&l4[r >> 2])[r & 3];
+        x[r] = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
+      }
+      if (!full)   // uniform
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int o = 8 * (r >> 2) + (r & 3);
-              x[r] = ((o >= lo) & (o <= hi)) ? x[r] : -INFINITY;
-            }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int o = 8 * (r >> 2) + (r & 3);
+          x[r] = ((o >= lo) & (o <= hi)) ? x[r] : -INFINITY;
         }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(x[r]);
+      if constexpr (!DK) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 0] * a.p_range, p[4 * q4 + 1] * a.p_range, 0, false);
           v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 2] * a.p_range, p[4 * q4 + 3] * a.p_range, v, true);
           pb[4 * sub + q4] = v;
         }
+      } else {
         i32x16 dP = {};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
-          dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tdo, st, kk, col, hh), vcode[2 * kk], dP, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tdo, sub, kk, col, hh), vcode[kk], dP, 0, 0, 0);
         float4 dsc4[4], d4[4];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          dsc4[a4] = *reinterpret_cast<const float4*>(tds + 32 * st + 4 * hh + 8 * a4);
-          d4[a4] = *reinterpret_cast<const float4*>(td + 32 * st + 4 * hh + 8 * a4);
+          dsc4[a4] = *reinterpret_cast<const float4*>(tds + base_it + 8 * a4);
+          d4[a4] = *reinterpret_cast<const float4*>(td + base_it + 8 * a4);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float dsc = reinterpret_cast<const float*>(&dsc4[r >> 2])[r & 3];
           const float dr = reinterpret_cast<const float*>(&d4[r >> 2])[r & 3];
-          const float tdp = static_cast<float>(dP[r]) * (dsc * sv_j) - dr;
-          ds[sub][r] = p[r] * tdp;     // p is 0 wherever the entry is masked
+          ds[sub][r] = p[r] * (static_cast<float>(dP[r]) * (dsc * sv_j) - dr);   // 0 wherever p is
         }
       }
+    }
+    if constexpr (!DK) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm64(t8, c, col, hh), pb, acc[c], 0, 0, 0, 0, 0, 0);
+    } else {
       const int e = e8m0_exponent(amax32(ds));
       const i32x8 db = pack_e4m3(ds, e);
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        accv[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm(tdo8, kc, c, col, hh), pb, accv[c], 0, 0, 0,
-                                                                  0, 0, 0);
-        acck[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm(tq8, kc, c, col, hh), db, acck[c], 0, 0, 0,
-                                                                  127, 0, e + 127);
-      }
+      for (int c = 0; c < CT; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag_cm64(t8, c, col, hh), db, acc[c], 0, 0, 0, 127, 0,
+                                                                 e + 127);
     }
-    if (more) put_scalars(cur ^ 1);
-    // the next tile's copies and scalars are in place, and every wave is done with this tile's slot
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
+  // the copies past the end write LDS: they complete before the work-group ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (kj < a.N) {
-    const float* sq = a.q8_scale + static_cast<int64_t>(bh) * D;
-    const float* sdo = a.do8_scale + static_cast<int64_t>(bh) * D;
-    const float inv_pr = 1.f / a.p_range;
-    float* outk = a.dk + (static_cast<int64_t>(bh) * a.N + kj) * D;
-    float* outv = a.dv + (static_cast<int64_t>(bh) * a.N + kj) * D;
+    const float* s8 = (DK ? a.q8_scale : a.do8_scale) + static_cast<int64_t>(bh) * D;
+    const float f = DK ? a.sm_scale : 1.f / a.p_range;
+    float* out = (DK ? a.dk : a.dv) + (static_cast<int64_t>(bh) * a.N + kj) * D;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int c0 = 32 * c + 8 * a4 + 4 * hh;
-        float4 ok, ov;
-        ok.x = acck[c][4 * a4 + 0] * (a.sm_scale * sq[c0 + 0]);
-        ok.y = acck[c][4 * a4 + 1] * (a.sm_scale * sq[c0 + 1]);
-        ok.z = acck[c][4 * a4 + 2] * (a.sm_scale * sq[c0 + 2]);
-        ok.w = acck[c][4 * a4 + 3] * (a.sm_scale * sq[c0 + 3]);
-        ov.x = accv[c][4 * a4 + 0] * (sdo[c0 + 0] * inv_pr);
-        ov.y = accv[c][4 * a4 + 1] * (sdo[c0 + 1] * inv_pr);
-        ov.z = accv[c][4 * a4 + 2] * (sdo[c0 + 2] * inv_pr);
-        ov.w = accv[c][4 * a4 + 3] * (sdo[c0 + 3] * inv_pr);
-        *reinterpret_cast<float4*>(outk + c0) = ok;
-        *reinterpret_cast<float4*>(outv + c0) = ov;
+        float4 o;
+        o.x = acc[c][4 * a4 + 0] * (f * s8[c0 + 0]);
+        o.y = acc[c][4 * a4 + 1] * (f * s8[c0 + 1]);
+        o.z = acc[c][4 * a4 + 2] * (f * s8[c0 + 2]);
+        o.w = acc[c][4 * a4 + 3] * (f * s8[c0 + 3]);
+        *reinterpret_cast<float4*>(out + c0) = o;
       }
   }
 }
@@ -623,7 +616,8 @@ hipError_t bwd_impl(const Problem& p, const BwdBuffers& bb, int causal, hipStrea
   a.p_range = p.p_range;
   const dim3 grid(p.nblk * p.B * p.H);
   hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 1>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, 2>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
