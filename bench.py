@@ -32,7 +32,6 @@ PEAK_PV16_TOPS = 2.0 / (1.0 / PEAK_TOPS + 1.0 / PEAK_BF16_TOPS)
 PEAK_FP4_TOPS = 10100.0 # MI355X dense FP4 and FP6 matrix peak
 # With MXFP4 Q and K, QK^T runs at the FP4 rate and P~V at the FP8 one.
 PEAK_MXFP4_TOPS = 2.0 / (1.0 / PEAK_FP4_TOPS + 1.0 / PEAK_TOPS)
-HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30    # calibration copy: reads and writes this many bytes
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
@@ -62,6 +61,31 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+QUANT_COUNTERS = os.path.join(ROOT, "profiles", "quant_counters.json")
+
+
+def quant_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("quant.hip", "sage_internal.h"):
+        with open(os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def quant_traffic_from_profile(workload: str):
+    """HBM bytes per call of the two quantisation calls ({"quant_qk": B, "quant_v": B})
+    from the committed rocprofv3 counter summary, or None when it is missing or
+    the kernels changed since."""
+    try:
+        with open(QUANT_COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != quant_source_hash() or rec.get("workload") != workload:
+        return None
+    return {c: v["hbm_bytes"] for c, v in rec.get("calls", {}).items()}
 
 
 def traffic_from_profile(workload: str):
@@ -387,6 +411,7 @@ def main():
     # P~V at the FP8 rate, half the operations each)
     peak = PEAK_PV16_TOPS if pv16 else (PEAK_MXFP4_TOPS if (mx or args.qk == "int_e2m3") else PEAK_TOPS)
     traffic = None if (pv16 or mx or args.qk != "int") else traffic_from_profile(w.name)
+    qtraffic = None if (pv16 or mx or args.qk != "int") else quant_traffic_from_profile(w.name)
     qk_bytes, v_bytes = quant_bytes(w, args.pv, args.qk)
     rec = {
         "metric": "attention TOPS (4*B*H*N^2*d, halved if causal) of quant_qk + quant_v + attn_fwd",
@@ -416,9 +441,11 @@ def main():
         "quant_roofline": {
             "bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "quant_qk": {"bytes": qk_bytes, "achieved": round(qk_bytes / (qk_ms * 1e6), 1),
-                         "frac": round(qk_bytes / (qk_ms * 1e6) / PEAK_HBM_GBPS, 4)},
+                         "frac": round(qk_bytes / (qk_ms * 1e6) / PEAK_HBM_GBPS, 4),
+                         "traffic": (qtraffic or {}).get("quant_qk")},
             "quant_v": {"bytes": v_bytes, "achieved": round(v_bytes / (v_ms * 1e6), 1),
-                        "frac": round(v_bytes / (v_ms * 1e6) / PEAK_HBM_GBPS, 4)},
+                        "frac": round(v_bytes / (v_ms * 1e6) / PEAK_HBM_GBPS, 4),
+                        "traffic": (qtraffic or {}).get("quant_v")},
         },
     }
     rec["accuracy"] = None
