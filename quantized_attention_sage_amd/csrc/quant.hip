@@ -122,28 +122,74 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
                                                float* __restrict__ scale_blk) {
   constexpr int TOK = Tile<D>::TOK, TPR = Tile<D>::TPR;
   const int t = threadIdx.x, g = t / TPR, cg = t % TPR;
-  if (t < 128) gmax[t] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < TOK; ++u) {
-    float ra = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(xs[u][e]));
-#pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) ra = fmaxf(ra, __shfl_xor(ra, m));
-    const int r = g * TOK + u;
-    const int grp = IS_Q ? q_group_in_block(gran, r) : k_group_in_block(gran, r);
-    if (cg == 0) atomicMax(&gmax[grp], __float_as_uint(ra));  // non-negative floats order as unsigned
-  }
-  __syncthreads();
   const float qm = static_cast<float>(qmax);
-  const int ng = IS_Q ? q_groups_per_block(gran) : k_groups_per_block(gran);
-  if (t < ng) scale_blk[t] = __uint_as_float(gmax[t]) / qm;
+  // Group maxima of this thread's rows.  THREAD granularity: every group lies
+  // inside one wave (a Q group is one row; a K group is one half of the
+  // wave's 32-key subtile), so lane exchanges finish it.  Otherwise the
+  // groups span waves and meet in LDS.
+  float am_row[TOK];
+  if (gran == SAGE_GRAN_THREAD) {
+    if constexpr (IS_Q) {
+#pragma unroll
+      for (int u = 0; u < TOK; ++u) {
+        float ra = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(xs[u][e]));
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) ra = fmaxf(ra, __shfl_xor(ra, m));
+        am_row[u] = ra;
+        if (cg == 0) scale_blk[g * TOK + u] = ra / qm;
+      }
+    } else {
+      // rows r of key group half (r & 7) >> 2 of the wave's subtile r >> 5
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < TOK; ++u) {
+        float ra = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(xs[u][e]));
+        if ((((g * TOK + u) & 7) >> 2) == 0) a0 = fmaxf(a0, ra);
+        else a1 = fmaxf(a1, ra);
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        a0 = fmaxf(a0, __shfl_xor(a0, m));
+        a1 = fmaxf(a1, __shfl_xor(a1, m));
+      }
+#pragma unroll
+      for (int u = 0; u < TOK; ++u) am_row[u] = (((g * TOK + u) & 7) >> 2) == 0 ? a0 : a1;
+      if ((t & 63) == 0) {
+        scale_blk[2 * (t >> 6)] = a0 / qm;
+        scale_blk[2 * (t >> 6) + 1] = a1 / qm;
+      }
+    }
+  } else {
+    if (t < 128) gmax[t] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TOK; ++u) {
+      float ra = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(xs[u][e]));
+#pragma unroll
+      for (int m = 1; m < TPR; m <<= 1) ra = fmaxf(ra, __shfl_xor(ra, m));
+      const int r = g * TOK + u;
+      const int grp = IS_Q ? q_group_in_block(gran, r) : k_group_in_block(gran, r);
+      if (cg == 0) atomicMax(&gmax[grp], __float_as_uint(ra));  // non-negative floats order as unsigned
+    }
+    __syncthreads();
+    const int ng = IS_Q ? q_groups_per_block(gran) : k_groups_per_block(gran);
+    if (t < ng) scale_blk[t] = __uint_as_float(gmax[t]) / qm;
+#pragma unroll
+    for (int u = 0; u < TOK; ++u) {
+      const int r = g * TOK + u;
+      am_row[u] = __uint_as_float(gmax[IS_Q ? q_group_in_block(gran, r) : k_group_in_block(gran, r)]);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < TOK; ++u) {
     const int r = g * TOK + u;
-    const int grp = IS_Q ? q_group_in_block(gran, r) : k_group_in_block(gran, r);
-    const float am = __uint_as_float(gmax[grp]);
+    const float am = am_row[u];
     const float inv = am > 0.f ? qm / am : 0.f;
     // code = clamp(rint(x' * inv)) as an exact small integer in fp32, then its
     // low byte; four bytes per word, assembled with byte permutes.
