@@ -37,6 +37,58 @@ struct Tile {
   static_assert(TOK >= 1 && (TOK & (TOK - 1)) == 0, "tokens per thread must be a power of two");
 };
 
+// Lane exchanges on the vector ALU instead of the LDS crossbar
+// (ds_bpermute).  xor_combine<M>(x, op) = op(x of lane l, x of lane l ^ M) on
+// every lane, for M = 1, 2 (quad permutes), 8 (a rotation by 8 inside each
+// row of 16 lanes), 16 and 32 (the permlane swaps, which deliver the two
+// values of a pair to both of its lanes).  op must be commutative (+, max,
+// min): both lanes of a pair then hold identical bits.
+template <int M, typename Op>
+__device__ __forceinline__ float xor_combine(float x, Op op) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    static_assert(M == 1 || M == 2 || M == 8, "lane distance without a one-instruction exchange");
+    constexpr int kCtrl = M == 1 ? 0xB1 : (M == 2 ? 0x4E : 0x128);   // quad_perm [1,0,3,2], [2,3,0,1]; row_ror:8
+    return op(x, __uint_as_float(static_cast<uint32_t>(
+                     __builtin_amdgcn_update_dpp(0, static_cast<int>(u), kCtrl, 0xf, 0xf, false))));
+  }
+}
+struct FAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+struct FMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct FMin { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+
+// Maximum over the L = 8 or 16 lanes of a row group (l / L equal): the two
+// quad exchanges, then the mirror inside 8 lanes and inside 16 (after the
+// quads agree, a mirrored partner holds the other quad's maximum).
+template <int L>
+__device__ __forceinline__ float row_max(float x) {
+  static_assert(L == 8 || L == 16, "row groups of 8 or 16 lanes");
+  x = xor_combine<1>(x, FMax{});
+  x = xor_combine<2>(x, FMax{});
+  x = fmaxf(x, __uint_as_float(static_cast<uint32_t>(
+                   __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(x)), 0x141, 0xf, 0xf, false))));
+  if constexpr (L == 16)
+    x = fmaxf(x, __uint_as_float(static_cast<uint32_t>(
+                     __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(x)), 0x140, 0xf, 0xf, false))));
+  return x;
+}
+
+// op over the token groups of a wave that hold the same channels (lanes
+// l ^ TPR, l ^ 2 TPR, ..., l ^ 32), in that order.
+template <int TPR, typename Op>
+__device__ __forceinline__ float across_rows(float x, Op op) {
+  static_assert(TPR == 8 || TPR == 16, "8 or 16 lanes per token row");
+  if constexpr (TPR == 8) x = xor_combine<8>(x, op);
+  x = xor_combine<16>(x, op);
+  return xor_combine<32>(x, op);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float to_f32(uint16_t b) {
   if constexpr (BF16) {
@@ -85,9 +137,7 @@ __device__ __forceinline__ void block_tree_sum(const float (&x)[Tile<D>::TOK][8]
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = v[0][e];
 #pragma unroll
-  for (int m = TPR; m < 64; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = s[e] + __shfl_xor(s[e], m);
+  for (int e = 0; e < 8; ++e) s[e] = across_rows<TPR>(s[e], FAdd{});
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64, cg = threadIdx.x % TPR;
   if (lane < TPR)
 #pragma unroll
@@ -135,8 +185,7 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
         float ra = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(xs[u][e]));
-#pragma unroll
-        for (int m = 1; m < TPR; m <<= 1) ra = fmaxf(ra, __shfl_xor(ra, m));
+        ra = row_max<TPR>(ra);
         am_row[u] = ra;
         if (cg == 0) scale_blk[g * TOK + u] = ra / qm;
       }
@@ -151,11 +200,8 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
         if ((((g * TOK + u) & 7) >> 2) == 0) a0 = fmaxf(a0, ra);
         else a1 = fmaxf(a1, ra);
       }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        a0 = fmaxf(a0, __shfl_xor(a0, m));
-        a1 = fmaxf(a1, __shfl_xor(a1, m));
-      }
+      a0 = xor_combine<32>(xor_combine<16>(row_max<16>(a0), FMax{}), FMax{});
+      a1 = xor_combine<32>(xor_combine<16>(row_max<16>(a1), FMax{}), FMax{});
 #pragma unroll
       for (int u = 0; u < TOK; ++u) am_row[u] = (((g * TOK + u) & 7) >> 2) == 0 ? a0 : a1;
       if ((t & 63) == 0) {
@@ -171,8 +217,7 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
       float ra = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ra = fmaxf(ra, fabsf(xs[u][e]));
-#pragma unroll
-      for (int m = 1; m < TPR; m <<= 1) ra = fmaxf(ra, __shfl_xor(ra, m));
+      ra = row_max<TPR>(ra);
       const int r = g * TOK + u;
       const int grp = IS_Q ? q_group_in_block(gran, r) : k_group_in_block(gran, r);
       if (cg == 0) atomicMax(&gmax[grp], __float_as_uint(ra));  // non-negative floats order as unsigned
@@ -284,8 +329,7 @@ __device__ __forceinline__ void quantize_block_mx(const float (&xs)[Tile<D>::TOK
     float am = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xs[u][e]));
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
+    am = xor_combine<2>(xor_combine<1>(am, FMax{}), FMax{});
     const uint32_t bits = __float_as_uint(am);
     const int ef = static_cast<int>((bits >> 23) & 0xffu);
     int s = ef - 127 - ((bits & 0x7fffffu) <= 0x400000u ? 2 : 1);
@@ -698,12 +742,10 @@ __global__ __launch_bounds__(kThreads) void v_stats_kernel(VArgs a) {
     }
   }
 #pragma unroll
-  for (int m = Tile<D>::TPR; m < 64; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], m));
-      mn[e] = fminf(mn[e], __shfl_xor(mn[e], m));
-    }
+  for (int e = 0; e < 8; ++e) {
+    mx[e] = across_rows<Tile<D>::TPR>(mx[e], FMax{});
+    mn[e] = across_rows<Tile<D>::TPR>(mn[e], FMin{});
+  }
   const int w = t / 64, lane = t % 64;
   if (lane < Tile<D>::TPR)
 #pragma unroll
