@@ -119,7 +119,9 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ base, in
 // pairs over each thread's TOK consecutive tokens, lane butterflies over
 // neighbouring token groups (fp32 addition is commutative, so both partners
 // hold identical bits), then the four 32-token wave sums as (w0+w1)+(w2+w3).
-// On return every thread holds the sums of its 8 channels.  lds: 4*D floats.
+// On return every thread holds the sums of its 8 channels.  lds: 4*D floats,
+// read after the one barrier and never written again by any caller (each
+// kernel forms one tree sum), so no barrier follows the reads.
 template <int D>
 __device__ __forceinline__ void block_tree_sum(const float (&x)[Tile<D>::TOK][8], float (&s)[8], float* lds) {
   constexpr int TOK = Tile<D>::TOK, TPR = Tile<D>::TPR;
@@ -148,7 +150,6 @@ __device__ __forceinline__ void block_tree_sum(const float (&x)[Tile<D>::TOK][8]
     const int c = 8 * cg + e;
     s[e] = (lds[c] + lds[D + c]) + (lds[2 * D + c] + lds[3 * D + c]);
   }
-  __syncthreads();
 }
 
 // Group of row r (0..127 inside a block) and the number of groups per block.
