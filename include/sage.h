@@ -113,7 +113,8 @@ typedef enum { SAGE_QK_INT = 0, SAGE_QK_MXFP4 = 1, SAGE_QK_INT_E4M3 = 2, SAGE_QK
 /* Shape of Q, K, V ([B, H, N, d], element type dtype).  Strides are in
  * elements for the B, H and N dimensions; the d dimension is contiguous.
  * Every stride must be a multiple of 8 and every tensor pointer 16-byte
- * aligned.  Supported: d in {64, 128}; 1 <= N <= 2^20; B, H >= 1. */
+ * aligned; the N stride must be below 2^22 elements (SAGE_EUNSUPPORTED
+ * otherwise).  Supported: d in {64, 128}; 1 <= N <= 2^20; B, H >= 1. */
 typedef struct {
   int64_t B, H, N, d;
   int32_t dtype;         /* sage_dtype, shared by Q, K, V and O */
@@ -237,7 +238,7 @@ SAGE_API sage_status sage_quant_v(const void* v, const sage_shape* s, const sage
  * Preliminary": FlashAttention-based tiled online softmax; INT8 matrix cores
  * for QK^T, FP8 matrix cores for P~V).  causal != 0 masks key j > query i.
  * o: [B, H, N, d] of the shape's dtype with element strides o_stride[0..2]
- * (multiples of 8; 16-byte aligned pointer). */
+ * (multiples of 8, the N stride below 2^22; 16-byte aligned pointer). */
 SAGE_API sage_status sage_attn_fwd(const sage_qk_buffers* qk, const sage_v_buffers* vb, const sage_shape* s,
                                    const sage_params* p, int causal, void* o, const int64_t o_stride[3],
                                    void* stream);

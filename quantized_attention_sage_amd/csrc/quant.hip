@@ -98,17 +98,30 @@ __device__ __forceinline__ float to_f32(uint16_t b) {
   }
 }
 
+// Raw buffer resource over `bytes` bytes from p, and its 16-byte loads: a
+// load at a byte offset at or past `bytes` returns zeros.  Rows past N are
+// read through it with no guard; a guarded load compiles to a branch whose
+// result is waited for before the next load is issued, which serialises a
+// block's loads.  bytes < 2^31 (the N stride limit keeps 128 rows below it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Load rows [row0, row0 + 128) of one head; rows >= N read as 0.
 template <int D, bool BF16>
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ base, int64_t sN, int row0, int N,
                                            float (&x)[Tile<D>::TOK][8]) {
   const int t = threadIdx.x;
   const int g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
+  const auto rs = rows_rsrc(base + static_cast<int64_t>(row0) * sN, static_cast<int64_t>(min(128, N - row0)) * sN * 2);
 #pragma unroll
   for (int u = 0; u < Tile<D>::TOK; ++u) {
-    const int r = row0 + g * Tile<D>::TOK + u;
-    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-    if (r < N) raw = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * sN + 8 * cg);
+    const int r = g * Tile<D>::TOK + u;
+    const uint4 raw = load16(rs, r * static_cast<int>(sN) * 2 + 16 * cg);
     const uint16_t* hv = reinterpret_cast<const uint16_t*>(&raw);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[u][e] = to_f32<BF16>(hv[e]);
@@ -451,13 +464,19 @@ __device__ __forceinline__ float segment_tree_sum(int n, int c32, int seg, F lea
         float v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+          // the index is clamped so that every load is issued unconditionally
+          // (a guarded load would wait for the one before it)
           const int i = first + i0 + u;
-          v[u] = i < n ? leaf(i) : 0.f;
+          const float lv = leaf(min(i, n - 1));
+          v[u] = i < n ? lv : 0.f;
         }
         push(((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
       }
     } else {
-      for (int i = first; i < first + L; ++i) push(i < n ? leaf(i) : 0.f);
+      for (int i = first; i < first + L; ++i) {
+        const float lv = leaf(min(i, n - 1));
+        push(i < n ? lv : 0.f);
+      }
     }
     result = stk[seg][c32][0];
     segsum[seg][c32] = result;
@@ -500,7 +519,7 @@ __global__ __launch_bounds__(256) void k_mean_kernel(QKArgs a) {
     for (int qb0 = seg; qb0 < a.nblk; qb0 += 64) {
       float mu[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) mu[u] = qb0 + 8 * u < a.nblk ? qm[static_cast<int64_t>(qb0 + 8 * u) * D] : 0.f;
+      for (int u = 0; u < 8; ++u) mu[u] = qm[static_cast<int64_t>(min(qb0 + 8 * u, a.nblk - 1)) * D];   // unused past nblk
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         uint32_t hi, lo;
@@ -552,16 +571,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // The first chunk of split-mean words is fetched before the quantisation,
   // so that its latency overlaps it.
   uint4 mq[PPT][2];
+  const auto mu_rs = rows_rsrc(musplit, static_cast<int64_t>(a.nblk) * D * 4);
   auto fetch_mu = [&](int qc0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int piece = t + kThreads * i;
       const int row = piece / (D / 8), c8 = piece % (D / 8);
-      mq[i][0] = mq[i][1] = make_uint4(0u, 0u, 0u, 0u);
-      if (qc0 + row < a.nblk) {
-        mq[i][0] = *reinterpret_cast<const uint4*>(musplit + static_cast<int64_t>(qc0 + row) * D + 8 * c8);
-        mq[i][1] = *reinterpret_cast<const uint4*>(musplit + static_cast<int64_t>(qc0 + row) * D + 8 * c8 + 4);
-      }
+      const int w0 = 4 * ((qc0 + row) * D + 8 * c8);   // rows past nblk read as zeros
+      mq[i][0] = load16(mu_rs, w0);
+      mq[i][1] = load16(mu_rs, w0 + 16);
     }
   };
   if (a.with_bias) fetch_mu(0);
@@ -596,11 +614,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   {
     const bool ok = key < valid;
     uint4 kraw[D / 16];
+    const auto krs = rows_rsrc(kin + static_cast<int64_t>(row0) * a.ksN, static_cast<int64_t>(valid) * a.ksN * 2);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kraw[ks] = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) kraw[ks] = *reinterpret_cast<const uint4*>(kin + static_cast<int64_t>(row0 + key) * a.ksN + 16 * ks + 8 * hh);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)   // keys past N read as zeros (and are masked below)
+      kraw[ks] = load16(krs, key * static_cast<int>(a.ksN) * 2 + 32 * ks + 16 * hh);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int c0 = 16 * ks + 8 * hh;
@@ -778,9 +795,22 @@ __global__ __launch_bounds__(256) void v_finalize_kernel(VArgs a) {
   const int bh = blockIdx.y, c32 = threadIdx.x & 31, c = 32 * blockIdx.x + c32, seg = threadIdx.x >> 5;
   float* part = a.out.v_partial + static_cast<int64_t>(bh) * a.nblk * 3 * D;
   float vmax = -INFINITY, vmin = INFINITY;
-  for (int i = seg; i < a.nblk; i += 8) {
-    vmax = fmaxf(vmax, part[static_cast<int64_t>(i) * 3 * D + D + c]);
-    vmin = fminf(vmin, part[static_cast<int64_t>(i) * 3 * D + 2 * D + c]);
+  // blocks seg, seg + 8, ..., eight at a time with every load issued before
+  // the first is used; indices past the last block re-read it (max and min
+  // are idempotent)
+  for (int i0 = seg; i0 < a.nblk; i0 += 64) {
+    float hx[8], lx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t i = min(i0 + 8 * j, a.nblk - 1);
+      hx[j] = part[i * 3 * D + D + c];
+      lx[j] = part[i * 3 * D + 2 * D + c];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vmax = fmaxf(vmax, hx[j]);
+      vmin = fminf(vmin, lx[j]);
+    }
   }
   mx[seg][c32] = vmax;
   mn[seg][c32] = vmin;
@@ -869,6 +899,7 @@ __global__ __launch_bounds__(kThreads) void v_pack16_kernel(VArgs a) {
   const int row0 = blk * 128;
   const int t = threadIdx.x, g = t / Tile<D>::TPR, cg = t % Tile<D>::TPR;
   const uint16_t* base = a.v + b * a.sB + h * a.sH;
+  const auto rs = rows_rsrc(base + static_cast<int64_t>(row0) * a.sN, static_cast<int64_t>(min(128, a.N - row0)) * a.sN * 2);
   // Four consecutive tokens 4k..4k+3 keep consecutive positions (only bits 2
   // and 3 swap), so each thread writes them per channel as one 8-byte word.
 #pragma unroll
@@ -876,9 +907,8 @@ __global__ __launch_bounds__(kThreads) void v_pack16_kernel(VArgs a) {
     uint4 raw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = row0 + g * Tile<D>::TOK + u4 + j;
-      raw[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < a.N) raw[j] = *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(r) * a.sN + 8 * cg);
+      const int r = g * Tile<D>::TOK + u4 + j;   // rows past N read as zeros
+      raw[j] = load16(rs, r * static_cast<int>(a.sN) * 2 + 16 * cg);
     }
     const int k = g * Tile<D>::TOK + u4;
     const int pos = (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);

@@ -67,6 +67,9 @@ sage_status check_shape(const sage_shape* s) {
   for (int i = 0; i < 3; ++i)
     for (int j = 0; j < 3; ++j)
       if (st[i][j] <= 0 || st[i][j] % 8 != 0) return fail(SAGE_EINVAL, "strides must be positive multiples of 8 elements");
+  for (int i = 0; i < 3; ++i)
+    if (st[i][2] >= sage::kMaxRowStride)
+      return fail(SAGE_EUNSUPPORTED, "N strides must be below 2^22 elements (got %lld)", (long long)st[i][2]);
   return SAGE_OK;
 }
 
@@ -125,6 +128,7 @@ sage_status check_out(const void* o, const int64_t* os) {
   if (!os) return fail(SAGE_EINVAL, "o_stride is NULL");
   for (int j = 0; j < 3; ++j)
     if (os[j] <= 0 || os[j] % 8 != 0) return fail(SAGE_EINVAL, "o strides must be positive multiples of 8 elements");
+  if (os[2] >= sage::kMaxRowStride) return fail(SAGE_EUNSUPPORTED, "the o N stride must be below 2^22 elements");
   return SAGE_OK;
 }
 

@@ -16,6 +16,11 @@ struct TensorView {
   int64_t sB, sH, sN;  // element strides
 };
 
+// Largest N stride (elements) of an input or output: the quantisation kernels
+// address a 128-row block through a buffer resource with 32-bit byte offsets,
+// and 128 rows of 2-byte elements then stay below 2^31 bytes.
+constexpr int64_t kMaxRowStride = int64_t(1) << 22;
+
 struct Problem {
   int B, H, N, D, n_pad, nblk;   // nblk = n_pad / 128
   int bf16;                      // 1: bfloat16 inputs/outputs, 0: float16

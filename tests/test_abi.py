@@ -125,6 +125,7 @@ def test_bind_workspace_checks():
 BAD_SHAPES = [
     dict(d=96), dict(N=0), dict(N=(1 << 20) + 1), dict(B=0), dict(dtype=7),
     dict(stride=(1000 * 128 * 2, 1000 * 128, 100)),      # N stride not a multiple of 8
+    dict(stride=(1000 * (1 << 22) * 2, 1000 * (1 << 22), 1 << 22)),   # N stride at the 2^22-element limit
 ]
 
 
