@@ -570,33 +570,56 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// D_i = sum_c dO_ic O_ic (fp32) of every padded row; 0 for rows >= N.  One
-// wave per row, 2 channels per lane.
+// D_i = sum_c dO_ic O_ic (fp32) of every padded row; 0 for rows >= N.  A
+// row is TPR = D/8 lanes of 8 channels (one 16-byte load of O and of dO
+// each), a work-group 256/TPR rows.  Both tensors are read through raw buffer
+// resources over the work-group's rows below N, so rows past N read as zeros
+// and every load issues unconditionally.  The row sum: the lane's 8 products,
+// then DPP exchanges inside the row's lanes.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(const uint16_t* o, const uint16_t* dout, int64_t sB, int64_t sH,
                                                        int64_t sN, int H, int N, int n_pad, float* dsum) {
-  const int t = threadIdx.x, l = t & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (t >> 6);   // n_pad / 4 blocks of 4 rows
+  constexpr int TPR = D / 8, RPW = 256 / TPR;
+  const int t = threadIdx.x, cg = t % TPR, rl = t / TPR;
+  const int row0 = static_cast<int>(blockIdx.x) * RPW;
   const int bh = static_cast<int>(blockIdx.y);
+  const int b = bh / H, h = bh % H;
+  const int64_t base = b * sB + h * sH + static_cast<int64_t>(row0) * sN;
+  const int64_t bytes = static_cast<int64_t>(max(0, min(RPW, N - row0))) * sN * 2;
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(o + base), 0, static_cast<int>(bytes), 0x00020000);
+  const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dout + base), 0, static_cast<int>(bytes), 0x00020000);
+  const int off = rl * static_cast<int>(sN) * 2 + 16 * cg;
+  const auto xo = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+  const auto xd = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
   float acc = 0.f;
-  if (r < N) {
-    const int b = bh / H, h = bh % H;
-    const int64_t off = b * sB + h * sH + r * sN;
-    for (int c = l; c < D; c += 64) {
-      float x, y;
-      if constexpr (BF16) {
-        x = __uint_as_float(static_cast<uint32_t>(o[off + c]) << 16);
-        y = __uint_as_float(static_cast<uint32_t>(dout[off + c]) << 16);
-      } else {
-        x = static_cast<float>(__builtin_bit_cast(_Float16, o[off + c]));
-        y = static_cast<float>(__builtin_bit_cast(_Float16, dout[off + c]));
-      }
-      acc = __builtin_fmaf(x, y, acc);
-    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t ho = static_cast<uint16_t>(xo[e / 2] >> (16 * (e & 1)));
+    const uint16_t hd = static_cast<uint16_t>(xd[e / 2] >> (16 * (e & 1)));
+    float x, y;
+    if constexpr (BF16) {
+      x = __uint_as_float(static_cast<uint32_t>(ho) << 16);
+      y = __uint_as_float(static_cast<uint32_t>(hd) << 16);
+    } else {
+      x = static_cast<float>(__builtin_bit_cast(_Float16, ho));
+      y = static_cast<float>(__builtin_bit_cast(_Float16, hd));
+    }
+    acc = __builtin_fmaf(x, y, acc);
   }
-  if (l == 0) dsum[static_cast<int64_t>(bh) * n_pad + r] = acc;
+  // sum over the row's TPR lanes: quad exchanges, then the mirrors inside 8 and 16 lanes
+  auto dpp_add = [](float v, int ctrl_sel) __attribute__((always_inline)) {
+    int u = __float_as_int(v), w;
+    if (ctrl_sel == 0) w = __builtin_amdgcn_update_dpp(0, u, 0xB1, 0xf, 0xf, false);        // quad_perm [1,0,3,2]
+    else if (ctrl_sel == 1) w = __builtin_amdgcn_update_dpp(0, u, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    else if (ctrl_sel == 2) w = __builtin_amdgcn_update_dpp(0, u, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    else w = __builtin_amdgcn_update_dpp(0, u, 0x140, 0xf, 0xf, false);                     // row_mirror
+    return v + __int_as_float(w);
+  };
+  acc = dpp_add(acc, 0);
+  acc = dpp_add(acc, 1);
+  acc = dpp_add(acc, 2);
+  if constexpr (TPR == 16) acc = dpp_add(acc, 3);
+  if (cg == 0) dsum[static_cast<int64_t>(bh) * n_pad + row0 + rl] = acc;
 }
 
 template <int D>
@@ -624,7 +647,7 @@ hipError_t bwd_impl(const Problem& p, const BwdBuffers& bb, int causal, hipStrea
 }  // namespace
 
 hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, float* dsum, hipStream_t st) {
-  const dim3 grid(p.n_pad / 4, p.B * p.H);
+  const dim3 grid(p.n_pad / (256 / (p.D / 8)), p.B * p.H);
   const uint16_t* op = static_cast<const uint16_t*>(o.ptr);
   const uint16_t* dp = static_cast<const uint16_t*>(dout.ptr);
   if (p.D == 128) {
