@@ -104,16 +104,23 @@ __global__ __launch_bounds__(256, 2) void exact_part_kernel(ExactArgs a) {
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1;
   // Load p of a sub-tile: key (t + 256 p) / (D/8), channels 8 ((t + 256 p) % (D/8)) ..; keys past ke read as 0.
+  // The loads go through raw buffer resources over the sub-tile's keys below
+  // ke (a load past the end returns zeros), so that none is guarded by a
+  // branch and all of them issue back to back.
   uint4 kp[PF], vp[PF];
   auto fetch = [&](int j0) __attribute__((always_inline)) {
+    const int64_t nk = max(0, min(KT, ke - j0));
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg + static_cast<int64_t>(j0) * a.ks2), 0,
+                                                      static_cast<int>(nk * a.ks2 * 2), 0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg + static_cast<int64_t>(j0) * a.vs2), 0,
+                                                      static_cast<int>(nk * a.vs2 * 2), 0x00020000);
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int idx = t + 256 * p, kk = idx / (D / 8), c = 8 * (idx % (D / 8)), j = j0 + kk;
-      kp[p] = vp[p] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < ke) {
-        kp[p] = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(j) * a.ks2 + c);
-        vp[p] = *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(j) * a.vs2 + c);
-      }
+      const int idx = t + 256 * p, kk = idx / (D / 8), c = 8 * (idx % (D / 8));
+      const auto xk = __builtin_amdgcn_raw_buffer_load_b128(rk, kk * static_cast<int>(a.ks2) * 2 + 2 * c, 0, 0);
+      const auto xv = __builtin_amdgcn_raw_buffer_load_b128(rv, kk * static_cast<int>(a.vs2) * 2 + 2 * c, 0, 0);
+      kp[p] = make_uint4(xk[0], xk[1], xk[2], xk[3]);
+      vp[p] = make_uint4(xv[0], xv[1], xv[2], xv[3]);
     }
   };
   if (kb < ke) fetch(kb);
