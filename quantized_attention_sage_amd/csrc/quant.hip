@@ -280,7 +280,11 @@ __device__ __forceinline__ void quantize_block(const float (&xs)[Tile<D>::TOK][8
       // bytes and write one 16-byte unit each.
       const uint32_t lo4 = c24[0] | (c24[1] << 24);
       const uint32_t hi2 = c24[1] >> 8;
-      const uint32_t lo_1 = __shfl_down(lo4, 1), hi_1 = __shfl_down(hi2, 1), lo_4 = __shfl_down(lo4, 4);
+      // the values of lanes l + 1 and l + 4 (inside the lane's 8-group, so a
+      // row shift of the 16-lane DPP row; the lanes past its end are unused)
+      const uint32_t lo_1 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo4), 0x101, 0xf, 0xf, false));
+      const uint32_t hi_1 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi2), 0x101, 0xf, 0xf, false));
+      const uint32_t lo_4 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo4), 0x104, 0xf, 0xf, false));
       const int j = cg / 8, m = cg % 8;
       uint8_t* row = reinterpret_cast<uint8_t*>(codes_blk) + static_cast<int64_t>(r) * D;
       if (m == 0 || m == 2) {          // slot bytes 0..15 -> unit 4j + h
