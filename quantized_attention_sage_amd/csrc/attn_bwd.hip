@@ -91,7 +91,7 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
   r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
   r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
   r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  r[3] = 0x00020000;
+  r[3] = kBufferWord3;
   return r;
 }
 
@@ -586,8 +586,8 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(const uint16_t* o, const 
   const int b = bh / H, h = bh % H;
   const int64_t base = b * sB + h * sH + static_cast<int64_t>(row0) * sN;
   const int64_t bytes = static_cast<int64_t>(max(0, min(RPW, N - row0))) * sN * 2;
-  const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(o + base), 0, static_cast<int>(bytes), 0x00020000);
-  const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dout + base), 0, static_cast<int>(bytes), 0x00020000);
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(o + base), 0, static_cast<int>(bytes), kBufferWord3);
+  const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(dout + base), 0, static_cast<int>(bytes), kBufferWord3);
   const int off = rl * static_cast<int>(sN) * 2 + 16 * cg;
   const auto xo = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
   const auto xd = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);

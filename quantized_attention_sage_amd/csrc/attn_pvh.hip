@@ -123,7 +123,7 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t bytes) {
   r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
   r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
   r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  r[3] = 0x00020000;
+  r[3] = kBufferWord3;
   return r;
 }
 

@@ -111,9 +111,9 @@ __global__ __launch_bounds__(256, 2) void exact_part_kernel(ExactArgs a) {
   auto fetch = [&](int j0) __attribute__((always_inline)) {
     const int64_t nk = max(0, min(KT, ke - j0));
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg + static_cast<int64_t>(j0) * a.ks2), 0,
-                                                      static_cast<int>(nk * a.ks2 * 2), 0x00020000);
+                                                      static_cast<int>(nk * a.ks2 * 2), kBufferWord3);
     const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg + static_cast<int64_t>(j0) * a.vs2), 0,
-                                                      static_cast<int>(nk * a.vs2 * 2), 0x00020000);
+                                                      static_cast<int>(nk * a.vs2 * 2), kBufferWord3);
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       const int idx = t + 256 * p, kk = idx / (D / 8), c = 8 * (idx % (D / 8));

@@ -104,7 +104,7 @@ __device__ __forceinline__ float to_f32(uint16_t b) {
 // result is waited for before the next load is issued, which serialises a
 // block's loads.  bytes < 2^31 (the N stride limit keeps 128 rows below it).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferWord3);
 }
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);

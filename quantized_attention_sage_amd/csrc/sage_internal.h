@@ -21,6 +21,11 @@ struct TensorView {
 // and 128 rows of 2-byte elements then stay below 2^31 bytes.
 constexpr int64_t kMaxRowStride = int64_t(1) << 22;
 
+// Word 3 of every raw buffer resource here: 32-bit data format, no swizzle,
+// no index stride (byte offsets; an access at or past the record count
+// returns zeros).
+constexpr int kBufferWord3 = 0x00020000;
+
 struct Problem {
   int B, H, N, D, n_pad, nblk;   // nblk = n_pad / 128
   int bf16;                      // 1: bfloat16 inputs/outputs, 0: float16
