@@ -28,15 +28,26 @@ def to_device(x: np.ndarray, dtype: str, layout: str = "bhnd"):
     """Upload exactly-representable float32 values as fp16/bf16.
 
     layout "bnhd" stores the tensor as [B, N, H, d] and returns the
-    [B, H, N, d] view (non-contiguous strides through the ABI).
+    [B, H, N, d] view (non-contiguous strides through the ABI); "widest_rows"
+    puts consecutive tokens WIDEST_ROW_STRIDE elements apart (the largest N
+    stride the library accepts), the rest of each row zero.
     """
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x)).to(torch_dtype(dtype))
     if layout == "bnhd":
         t = t.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    elif layout == "widest_rows":
+        B, H, N, d = t.shape
+        wide = torch.zeros((B, H, N, WIDEST_ROW_STRIDE), dtype=t.dtype, device="cuda")
+        wide[..., :d] = t.cuda()
+        t = wide[..., :d]
     else:
         t = t.cuda()
     return t
+
+
+# the largest N stride (elements) the library accepts: below 2^22, a multiple of 8
+WIDEST_ROW_STRIDE = (1 << 22) - 8
 
 
 # ------------------------------------------------------------------ guard bands

@@ -129,6 +129,12 @@ def test_strided_inputs():
     _check_case(scaled(WORKLOADS["llm_prefill"], B=2, H=2, N=333), layout="bnhd")
 
 
+def test_widest_row_stride():
+    # rows 2^22 - 8 elements apart (8 MiB each): the quantisers' 32-bit buffer
+    # offsets at their largest, with a ragged last block (130 = 128 + 2 rows)
+    _check_case(scaled(WORKLOADS["target"], B=1, H=1, N=130), layout="widest_rows")
+
+
 def test_repeatable_bits():
     w = scaled(WORKLOADS["target"], H=2, N=900)
     q, k, v = make_inputs(w)
