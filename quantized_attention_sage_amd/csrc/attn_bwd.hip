@@ -389,8 +389,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int ROWS = QH * D;                             // bytes of one row-major half tile
   constexpr int NT = DK ? 3 : 2;                           // code tiles per slot
   constexpr int AUX = NT * ROWS;                           // 4 x 64 floats of per-query scalars
-  constexpr int SLOT = AUX + 4 * 256;
-  constexpr int NC = NT * (D / 64) + 1;                    // copies per wave and half tile
+  constexpr int BIASB = AUX + 4 * 256;                     // the key block's bias row for the half tile's Q block
+  constexpr int SLOT = BIASB + 2 * 256;
+  constexpr int NC = NT * (D / 64) + 2;                    // copies per wave and half tile
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * SLOT];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
 
@@ -449,6 +450,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     else if (w == 1) dma4(rl, lane4, so, dst);
     else if (w == 2) dma4(rds, lane4, so, dst);
     else dma4(rd, lane4, so, dst);
+    // the bias of this block's 128 keys against the half tile's query block
+    // (512 bytes): waves 0 and 1 copy a half each, waves 2 and 3 the same
+    // halves again (identical bytes), so that every wave issues NC copies
+    // (a resource over that one bias row: a head's rows can pass 2^32 bytes)
+    const i32x4 rb = buffer_rsrc(a.bias + (static_cast<int64_t>(bh) * a.nblk + (q0 >> 7)) * a.n_pad,
+                                 static_cast<uint32_t>(a.n_pad) * 4u);
+    const uint32_t bh_off = 256u * static_cast<uint32_t>(w & 1);
+    dma4(rb, lane4 + bh_off, static_cast<uint32_t>(4 * k0), base + BIASB + bh_off);
   };
   copies(h0, 0);
   copies(h0 + 1, 1);
@@ -458,10 +467,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     // This wave's copies of half tile h are complete (only the NC of h + 1
     // may still run); after the barrier every wave's are, and every wave is
     // done with the slot of h - 1, which the copies of h + 2 refill.
-    if constexpr (NC == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(NC == 8 || NC == 6 || NC == 5 || NC == 4, "one wait per copy count");
+    if constexpr (NC == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (NC == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else if constexpr (NC == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (NC == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     copies(h + 2, (h + 2 - h0) % 3);
     const uint8_t* slot = lds + ((h - h0) % 3) * SLOT;
     const uint8_t* tq = slot;
@@ -472,7 +482,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     const float* tds = tqs + 128;
     const float* td = tqs + 192;
     const int q0 = h * QH;
-    const float bj = a.bias[(static_cast<int64_t>(bh) * a.nblk + (q0 >> 7)) * a.n_pad + kj];
+    // from the slot: a global load here would be waited for together with
+    // the copies issued just before it (the compiler cannot count those)
+    const float bj = reinterpret_cast<const float*>(slot + BIASB)[32 * w + col];
     // every entry of the half tile visible (uniform): no per-entry mask
     const bool full = q0 + QH <= a.N && k0 + kT <= a.N && (!a.causal || k0 + kT - 1 <= q0);
 
