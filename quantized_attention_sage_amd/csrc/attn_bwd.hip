@@ -28,6 +28,8 @@
 // ring filled by direct global-to-LDS copies two half tiles ahead.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "sage_internal.h"
 
 namespace sage {
@@ -68,6 +70,7 @@ struct BwdArgs {
   float scale_log2;         // sm_scale * log2(e)
   float sm_scale;
   float p_range;
+  float p_range_log2;       // log2(p_range): P P_r = 2^(s - L + log2 P_r)
 };
 
 // 16-byte chunk swizzle inside an LDS row (bank-conflict-free fragment reads;
@@ -315,6 +318,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const float* tks = tb + 64;
     const float* tvs = tb + 128;
     const int k0 = h * KH;
+    // every entry of the half tile visible (uniform): no per-entry mask
+    const bool full = q0 + kT <= a.N && k0 + KH <= a.N && (!a.causal || k0 + KH - 1 <= q0);
 
     float ds[2][16];
 #pragma unroll
@@ -334,11 +339,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       float4 b4[4];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) b4[a4] = *reinterpret_cast<const float4*>(tb + 32 * sub + 4 * hh + 8 * a4);
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        x[r] = static_cast<float>(S[r]) * cs + reinterpret_cast<const float*>(&b4[r >> 2])[r & 3] - Li;
+      if (!full)   // uniform
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = 8 * (r >> 2) + (r & 3) <= rel ? x[r] : -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = static_cast<float>(S[r]) * cs + reinterpret_cast<const float*>(&b4[r >> 2])[r & 3] - Li;
-        x = 8 * (r >> 2) + (r & 3) <= rel ? x : -INFINITY;
-        const float p = __builtin_amdgcn_exp2f(x);
+        const float p = __builtin_amdgcn_exp2f(x[r]);
         const float tdp = static_cast<float>(dP[r]) * cd - Di;
         ds[sub][r] = p * tdp;
       }
@@ -484,7 +494,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     const int q0 = h * QH;
     // from the slot: a global load here would be waited for together with
     // the copies issued just before it (the compiler cannot count those)
-    const float bj = reinterpret_cast<const float*>(slot + BIASB)[32 * w + col];
+    // (dV: P^ = E4M3(P P_r) with P P_r = 2^(s - L + log2 P_r), so log2 P_r
+    // rides on the key's bias and no product per entry is needed)
+    const float bj = reinterpret_cast<const float*>(slot + BIASB)[32 * w + col] + (DK ? 0.f : a.p_range_log2);
     // every entry of the half tile visible (uniform): no per-entry mask
     const bool full = q0 + QH <= a.N && k0 + kT <= a.N && (!a.causal || k0 + kT - 1 <= q0);
 
@@ -524,8 +536,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
       if constexpr (!DK) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 0] * a.p_range, p[4 * q4 + 1] * a.p_range, 0, false);
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 2] * a.p_range, p[4 * q4 + 3] * a.p_range, v, true);
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 0], p[4 * q4 + 1], 0, false);
+          v = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * q4 + 2], p[4 * q4 + 3], v, true);
           pb[4 * sub + q4] = v;
         }
       } else {
@@ -649,6 +661,7 @@ hipError_t bwd_impl(const Problem& p, const BwdBuffers& bb, int causal, hipStrea
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.sm_scale = p.sm_scale;
   a.p_range = p.p_range;
+  a.p_range_log2 = static_cast<float>(std::log2(static_cast<double>(p.p_range)));
   const dim3 grid(p.nblk * p.B * p.H);
   hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, 1>), grid, dim3(256), 0, st, a);
