@@ -231,6 +231,15 @@ __device__ __forceinline__ i32x8 frag_cm64(const uint8_t* tile, int c, int col, 
   return v;
 }
 
+// Work-group id -> item (head-major, then block).  Work-groups are dispatched
+// round-robin over the 8 XCDs, each with its own L2; regrouping consecutive
+// ids gives every XCD a contiguous run of items, so the rows that a head's
+// blocks all stream through their rings are fetched into one L2.
+__device__ __forceinline__ int xcd_item(int id, int total) {
+  constexpr int kXcd = 8;
+  return total % kXcd == 0 ? (id % kXcd) * (total / kXcd) + id / kXcd : id;
+}
+
 // dQ of one 128-query block.  Keys advance in 64-key half tiles through a
 // three-slot LDS ring: half tile h + 2 is copied straight from global memory
 // (buffer_load ... lds) while half tile h is used.  Each wave issues the same
@@ -250,8 +259,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int bh = static_cast<int>(blockIdx.x) / a.nblk;
-  int qb = static_cast<int>(blockIdx.x) % a.nblk;
+  const int item = xcd_item(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int bh = item / a.nblk;
+  int qb = item % a.nblk;
   if (a.causal) qb = a.nblk - 1 - qb;   // longest blocks first
   const int q0 = qb * kT, qi = q0 + 32 * w + col;
   const int64_t row = static_cast<int64_t>(bh) * a.n_pad + qi;
@@ -407,8 +417,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
 
   const int t = threadIdx.x, l = t & 63, col = l & 31, hh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int bh = static_cast<int>(blockIdx.x) / a.nblk;
-  const int kb = static_cast<int>(blockIdx.x) % a.nblk;   // causal: low blocks have the most queries, first
+  const int item = xcd_item(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int bh = item / a.nblk;
+  const int kb = item % a.nblk;   // causal: low blocks have the most queries, first
   const int k0 = kb * kT, kj = k0 + 32 * w + col;
   const int64_t krow = static_cast<int64_t>(bh) * a.n_pad + kj;
   const bool k_ok = kj < a.N;
