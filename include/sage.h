@@ -305,12 +305,14 @@ SAGE_API sage_status sage_attn_fwd_lse(const sage_qk_buffers* qk, const sage_v_b
  *   sage_v_buffers (codes uint8 [B,H,d,N_pad] in the permuted channel-major
  *   order, scale and mean fp32 [B,H,d]; k8 holds K' = K - mean(K) and its
  *   mean, do8 and q8 unsmoothed, means 0);  fp8_partial: their shared
- *   scratch;  dsum fp32 [B,H,N_pad]: D (0 past N). */
+ *   scratch;  dsum fp32 [B,H,N_pad]: D (0 past N);  lse_do and dsum_do
+ *   fp32 [B,H,N_pad]: L - log2 s and D / s of each row with the row's INT8 dO
+ *   scale s (+inf and 0 where s = 0), the dK kernel's per-row terms. */
 typedef struct {
   int64_t n_pad;
   sage_span do_codes, do_scale, do_mean, v_codes, v_scale, v_mean, v_partial;
   sage_span do8_codes, do8_scale, do8_mean, q8_codes, q8_scale, q8_mean, k8_codes, k8_scale, k8_mean;
-  sage_span fp8_partial, dsum;
+  sage_span fp8_partial, dsum, lse_do, dsum_do;
   size_t total_bytes;
 } sage_bwd_layout;
 

@@ -62,7 +62,7 @@ class Layout(ctypes.Structure):
 
 BWD_SPANS = ("do_codes", "do_scale", "do_mean", "v_codes", "v_scale", "v_mean", "v_partial",
              "do8_codes", "do8_scale", "do8_mean", "q8_codes", "q8_scale", "q8_mean", "k8_codes", "k8_scale",
-             "k8_mean", "fp8_partial", "dsum")
+             "k8_mean", "fp8_partial", "dsum", "lse_do", "dsum_do")
 
 
 class BwdLayout(ctypes.Structure):

@@ -209,6 +209,7 @@ class BwdWorkspace:
             "q8_codes": (torch.uint8, (B, H, d, n_pad)), "q8_scale": (torch.float32, (B, H, d)),
             "k8_codes": (torch.uint8, (B, H, d, n_pad)), "k8_scale": (torch.float32, (B, H, d)),
             "k8_mean": (torch.float32, (B, H, d)), "dsum": (torch.float32, (B, H, n_pad)),
+            "lse_do": (torch.float32, (B, H, n_pad)), "dsum_do": (torch.float32, (B, H, n_pad)),
         }
         dt, shp = shapes[name]
         return raw.view(dt).view(shp)

@@ -71,6 +71,8 @@ struct BwdArgs {
   float sm_scale;
   float p_range;
   float p_range_log2;       // log2(p_range): P P_r = 2^(s - L + log2 P_r)
+  const float* lse_do;      // L - log2 s_dO per row (+inf where s_dO = 0)
+  const float* dsum_do;     // D / s_dO per row (0 where s_dO = 0)
 };
 
 // 16-byte chunk swizzle inside an LDS row (bank-conflict-free fragment reads;
@@ -400,7 +402,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 //   dV^T += dO'^T P^ (P^ = E4M3(P P_r)): Q rows, dO' (E4M3) channel rows, Q
 //     scale and L per query.
 //   dK^T += Q'^T dS^ (dS^ = E4M3(dS 2^-e) per 64-query group): Q rows, dO
-//     rows, Q' (E4M3) channel rows, Q scale, dO scale, L and D per query.
+//     rows, Q' (E4M3) channel rows, Q scale, L - log2 s_dO and D / s_dO per
+//     query (the dO scale s_dO rides on P: see bwd_dsum_kernel).
 template <int D, int PART>
 __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr bool DK = PART == 2;
@@ -450,15 +453,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   const uint32_t head_f = static_cast<uint32_t>(a.n_pad * 4);
   const int64_t rbase = static_cast<int64_t>(bh) * a.n_pad;
   const i32x4 rqs = buffer_rsrc(a.q_scale + rbase, head_f);
-  const i32x4 rl = buffer_rsrc(a.lse + rbase, head_f);
-  const i32x4 rds = buffer_rsrc(a.do_scale + rbase, head_f);
-  const i32x4 rd = buffer_rsrc(a.dsum + rbase, head_f);
+  const i32x4 rl = buffer_rsrc((DK ? a.lse_do : a.lse) + rbase, head_f);
+  const i32x4 rd = buffer_rsrc(a.dsum_do + rbase, head_f);
   const uint32_t off_rows = rows_off<D>(t), off_cm = cm64_off(t, a.n_pad);
 
   const int h0 = a.causal ? 2 * kb : 0, nh = 2 * a.nblk;
   // Slot layout: Q rows, [dO rows,] the E4M3 channel rows (dO' for dV, Q' for
-  // dK), then 64 floats each of Q scale, L, dO scale and D (dV: the last two
-  // rows take spare copies of Q scale so that every wave issues NC copies).
+  // dK), then 64 floats each of Q scale, L (dK: L - log2 s_dO), a spare copy
+  // of the Q scale and D / s_dO (dV: the Q scale again), so that every wave
+  // issues NC copies.
   auto copies = [&](int h, int slot) __attribute__((always_inline)) {
     const int q0 = min(h, nh - 1) * QH;        // past the end: the last half tile again (never read)
     const uint32_t base = lds0 + slot * SLOT;
@@ -467,9 +470,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     copy_cm64<D>(base + (NT - 1) * ROWS, r8, off_cm, q0, a.n_pad, w);
     const uint32_t lane4 = 4u * static_cast<uint32_t>(l), so = static_cast<uint32_t>(4 * q0);
     const uint32_t dst = base + AUX + 256 * w;
-    if (w == 0 || (!DK && w != 1)) dma4(rqs, lane4, so, dst);
+    if (w == 0 || w == 2 || (!DK && w == 3)) dma4(rqs, lane4, so, dst);
     else if (w == 1) dma4(rl, lane4, so, dst);
-    else if (w == 2) dma4(rds, lane4, so, dst);
     else dma4(rd, lane4, so, dst);
     // the bias of this block's 128 keys against the half tile's query block
     // (512 bytes): waves 0 and 1 copy a half each, waves 2 and 3 the same
@@ -500,7 +502,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     const uint8_t* t8 = slot + (NT - 1) * ROWS;
     const float* tqs = reinterpret_cast<const float*>(slot + AUX);
     const float* tl = tqs + 64;
-    const float* tds = tqs + 128;
     const float* td = tqs + 192;
     const int q0 = h * QH;
     // from the slot: a global load here would be waited for together with
@@ -556,17 +557,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
           dP = __builtin_amdgcn_mfma_i32_32x32x32_i8(frag_rows<D>(tdo, sub, kk, col, hh), vcode[kk], dP, 0, 0, 0);
-        float4 dsc4[4], d4[4];
+        // p = P s_dO (the row's L - log2 s_dO in tl), so p (dP s_V - D / s_dO)
+        // = P (dP s_dO s_V - D) with no product of two scales per entry
+        float4 d4[4];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          dsc4[a4] = *reinterpret_cast<const float4*>(tds + base_it + 8 * a4);
-          d4[a4] = *reinterpret_cast<const float4*>(td + base_it + 8 * a4);
-        }
+        for (int a4 = 0; a4 < 4; ++a4) d4[a4] = *reinterpret_cast<const float4*>(td + base_it + 8 * a4);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float dsc = reinterpret_cast<const float*>(&dsc4[r >> 2])[r & 3];
           const float dr = reinterpret_cast<const float*>(&d4[r >> 2])[r & 3];
-          ds[sub][r] = p[r] * (static_cast<float>(dP[r]) * (dsc * sv_j) - dr);   // 0 wherever p is
+          ds[sub][r] = p[r] * (static_cast<float>(dP[r]) * sv_j - dr);   // 0 wherever p is
         }
       }
     }
@@ -605,7 +604,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// D_i = sum_c dO_ic O_ic (fp32) of every padded row; 0 for rows >= N.  A
+// D_i = sum_c dO_ic O_ic (fp32) of every padded row; 0 for rows >= N; and
+// from it, L_i and the row's INT8 dO scale, the dK kernel's per-row terms.  A
 // row is TPR = D/8 lanes of 8 channels (one 16-byte load of O and of dO
 // each), a work-group 256/TPR rows.  Both tensors are read through raw buffer
 // resources over the work-group's rows below N, so rows past N read as zeros
@@ -613,7 +613,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
 // then DPP exchanges inside the row's lanes.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(const uint16_t* o, const uint16_t* dout, int64_t sB, int64_t sH,
-                                                       int64_t sN, int H, int N, int n_pad, float* dsum) {
+                                                       int64_t sN, int H, int N, int n_pad, const float* do_scale,
+                                                       const float* lse, float* dsum, float* lse_do, float* dsum_do) {
   constexpr int TPR = D / 8, RPW = 256 / TPR;
   const int t = threadIdx.x, cg = t % TPR, rl = t / TPR;
   const int row0 = static_cast<int>(blockIdx.x) * RPW;
@@ -654,7 +655,15 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(const uint16_t* o, const 
   acc = dpp_add(acc, 1);
   acc = dpp_add(acc, 2);
   if constexpr (TPR == 16) acc = dpp_add(acc, 3);
-  if (cg == 0) dsum[static_cast<int64_t>(bh) * n_pad + row0 + rl] = acc;
+  if (cg == 0) {
+    const int64_t i = static_cast<int64_t>(bh) * n_pad + row0 + rl;
+    dsum[i] = acc;
+    // the dK kernel's per-row terms, with the row's INT8 dO scale s:
+    // 2^(s_ij - (L - log2 s)) (dP s_V - D / s) = P (dP s s_V - D)
+    const float sc = do_scale[i];
+    lse_do[i] = sc > 0.f ? lse[i] - log2f(sc) : INFINITY;
+    dsum_do[i] = sc > 0.f ? acc / sc : 0.f;
+  }
 }
 
 template <int D>
@@ -667,6 +676,7 @@ hipError_t bwd_impl(const Problem& p, const BwdBuffers& bb, int causal, hipStrea
   a.q8_codes = bb.q8.v_codes; a.q8_scale = bb.q8.v_scale;
   a.k8_codes = bb.k8.v_codes; a.k8_scale = bb.k8.v_scale;
   a.dsum = bb.dsum;
+  a.lse_do = bb.lse_do; a.dsum_do = bb.dsum_do;
   a.dq = bb.dq; a.dk = bb.dk; a.dv = bb.dv;
   a.H = p.H; a.N = p.N; a.n_pad = p.n_pad; a.nblk = p.nblk; a.causal = causal ? 1 : 0;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
@@ -682,17 +692,14 @@ hipError_t bwd_impl(const Problem& p, const BwdBuffers& bb, int causal, hipStrea
 
 }  // namespace
 
-hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, float* dsum, hipStream_t st) {
+hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, const BwdBuffers& bb, hipStream_t st) {
   const dim3 grid(p.n_pad / (256 / (p.D / 8)), p.B * p.H);
   const uint16_t* op = static_cast<const uint16_t*>(o.ptr);
   const uint16_t* dp = static_cast<const uint16_t*>(dout.ptr);
-  if (p.D == 128) {
-    if (p.bf16) hipLaunchKernelGGL((bwd_dsum_kernel<128, true>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
-    else hipLaunchKernelGGL((bwd_dsum_kernel<128, false>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
-  } else {
-    if (p.bf16) hipLaunchKernelGGL((bwd_dsum_kernel<64, true>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
-    else hipLaunchKernelGGL((bwd_dsum_kernel<64, false>), grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, dsum);
-  }
+  auto kernel = p.D == 128 ? (p.bf16 ? bwd_dsum_kernel<128, true> : bwd_dsum_kernel<128, false>)
+                           : (p.bf16 ? bwd_dsum_kernel<64, true> : bwd_dsum_kernel<64, false>);
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, op, dp, o.sB, o.sH, o.sN, p.H, p.N, p.n_pad, bb.dov.q_scale,
+                     bb.lse, bb.dsum, bb.lse_do, bb.dsum_do);
   return hipGetLastError();
 }
 

@@ -326,6 +326,8 @@ SAGE_API sage_status sage_bwd_workspace_layout(const sage_shape* s, const sage_p
   put(L.k8_mean, BH * D * 4);
   put(L.fp8_partial, BH * nblk * 3 * D * 4);
   put(L.dsum, BH * n_pad * 4);
+  put(L.lse_do, BH * n_pad * 4);
+  put(L.dsum_do, BH * n_pad * 4);
   L.total_bytes = off;
   *out = L;
   return ok();
@@ -373,6 +375,8 @@ SAGE_API sage_status sage_attn_bwd(const void* q, const void* k, const void* v, 
   bb.k8 = {reinterpret_cast<uint8_t*>(at(L.k8_codes)), reinterpret_cast<float*>(at(L.k8_scale)),
            reinterpret_cast<float*>(at(L.k8_mean)), fp8_partial};
   bb.dsum = reinterpret_cast<float*>(at(L.dsum));
+  bb.lse_do = reinterpret_cast<float*>(at(L.lse_do));
+  bb.dsum_do = reinterpret_cast<float*>(at(L.dsum_do));
   bb.dq = dq;
   bb.dk = dk;
   bb.dv = dv;
@@ -406,7 +410,7 @@ SAGE_API sage_status sage_attn_bwd(const void* q, const void* k, const void* v, 
       (e = sage::launch_quant_v(pc, dov, bb.do8, hs)) != hipSuccess ||
       (e = sage::launch_quant_v(pc, qv, bb.q8, hs)) != hipSuccess ||
       (e = sage::launch_quant_v(pk, kv, bb.k8, hs)) != hipSuccess ||
-      (e = sage::launch_bwd_dsum(pr, ov, dov, bb.dsum, hs)) != hipSuccess)
+      (e = sage::launch_bwd_dsum(pr, ov, dov, bb, hs)) != hipSuccess)
     return launch_result(e, "sage_attn_bwd (operands)");
   return launch_result(sage::launch_attn_bwd(pr, bb, causal, hs), "sage_attn_bwd");
 }

@@ -75,12 +75,16 @@ struct BwdBuffers {
   sage_v_buffers q8;      // E4M3 Q per channel (no smoothing)
   sage_v_buffers k8;      // E4M3 K' = K - mean(K) per channel
   float* dsum;            // D = rowsum(dO o O), [B, H, n_pad]
+  float* lse_do;          // L - log2 s_dO per row (+inf where s_dO = 0), [B, H, n_pad]
+  float* dsum_do;         // D / s_dO per row (0 where s_dO = 0), [B, H, n_pad]
   float* dq;
   float* dk;
   float* dv;              // fp32 [B, H, N, d], contiguous
 };
-// D of every padded row (0 past N); o and dout share the strides of `o`.
-hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, float* dsum, hipStream_t st);
+// D of every padded row (0 past N), and the dK kernel's per-row terms from D,
+// the forward's L and the INT8 dO scales (bb.dov.q_scale, written before);
+// o and dout share the strides of `o`.
+hipError_t launch_bwd_dsum(const Problem& p, TensorView o, TensorView dout, const BwdBuffers& bb, hipStream_t st);
 // dQ (one work-group per query block) and dK, dV (one per key block).
 hipError_t launch_attn_bwd(const Problem& p, const BwdBuffers& bb, int causal, hipStream_t st);
 

@@ -21,7 +21,7 @@ hipError_t launch_probe_reference(const Problem&, TensorView, TensorView, Tensor
   return hipErrorNotSupported;
 }
 hipError_t launch_probe_sums(const Problem&, int, char*, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_bwd_dsum(const Problem&, TensorView, TensorView, float*, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_bwd_dsum(const Problem&, TensorView, TensorView, const BwdBuffers&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attn_bwd(const Problem&, const BwdBuffers&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t static_workspace(void**, int*) { return hipErrorNotSupported; }
 

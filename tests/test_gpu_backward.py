@@ -110,7 +110,7 @@ def run_backward(w):
         x.check(n)
     gpu = {n: bws.view(n).cpu().numpy() for n in ("do_codes", "do_scale", "v_codes", "v_scale", "do8_codes",
                                                    "do8_scale", "q8_codes", "q8_scale", "k8_codes", "k8_scale",
-                                                   "dsum")}
+                                                   "dsum", "lse_do", "dsum_do")}
     return dict(q=q, k=k, v=v, do=do, o_em=o_em, lse_em=lse_em, qk_o=qk_o, vq_o=vq_o,
                 fwd_codes=(ws.view("q_codes").cpu().numpy(), ws.view("k_codes").cpu().numpy()),
                 lse_gpu=lse_gpu.cpu().numpy(), ops=gpu, grads=[x.t.cpu().numpy().astype(np.float64) for x in grads])
@@ -146,7 +146,18 @@ def test_backward_parity(case):
         np.testing.assert_array_equal(_bits(ops[f"{n}8_scale"]), _bits(ctx["fp8"][n]["v_scale"]),
                                       err_msg=f"E4M3 {n} scales")
     dd = np.abs(ops["dsum"].astype(np.float64) - ctx["D"])
-    assert np.all(dd <= 1e-6 * (np.abs(ctx["D"]) + np.abs(r["do"]).max() * np.abs(r["o_em"]).max())), float(dd.max())
+    d_tol = 1e-6 * (np.abs(ctx["D"]) + np.abs(r["do"]).max() * np.abs(r["o_em"]).max())
+    assert np.all(dd <= d_tol), float(dd.max())
+    # the dK kernel's per-row terms L - log2 s and D / s (s: the row's INT8 dO
+    # scale), from the oracle's L, D and scales; +inf and 0 where s = 0
+    s_do = dov["q_scale"].astype(np.float64)[:, :, :n_rows]
+    pos = s_do > 0
+    lse_do, dsum_do = ops["lse_do"][:, :, :n_rows], ops["dsum_do"][:, :, :n_rows]
+    want_l = r["lse_em"][:, :, :n_rows].astype(np.float64) - np.log2(np.where(pos, s_do, 1.0))
+    want_d = ctx["D"][:, :, :n_rows] / np.where(pos, s_do, 1.0)
+    assert np.all(np.abs(lse_do[pos] - want_l[pos]) <= 2.0 ** -20 * (1 + np.abs(want_l[pos])))
+    assert np.all(np.abs(dsum_do[pos] - want_d[pos]) <= d_tol[:, :, :n_rows][pos] / s_do[pos] + 2.0 ** -22 * np.abs(want_d[pos]))
+    assert np.all(np.isposinf(lse_do[~pos])) and np.all(dsum_do[~pos] == 0)
 
     em = ob.emulate_backward(ctx)
     ex = ob.exact_attention_grad(r["q"], r["k"], r["v"], r["do"], w.causal)
