@@ -398,14 +398,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // queries of a subtile in one lane.  Queries advance in 64-query half tiles
 // through a three-slot LDS ring filled by direct copies two half tiles ahead,
 // as in the dQ kernel (NC copies per wave and half tile, waited for by count).
-// One accumulator set per kernel keeps two work-groups on a CU.
+// One accumulator set per kernel keeps two work-groups on a CU (dV, with the
+// smaller ring and at most 168 registers: three).
 //   dV^T += dO'^T P^ (P^ = E4M3(P P_r)): Q rows, dO' (E4M3) channel rows, Q
 //     scale and L per query.
 //   dK^T += Q'^T dS^ (dS^ = E4M3(dS 2^-e) per 64-query group): Q rows, dO
 //     rows, Q' (E4M3) channel rows, Q scale, L - log2 s_dO and D / s_dO per
 //     query (the dO scale s_dO rides on P: see bwd_dsum_kernel).
 template <int D, int PART>
-__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, PART == 1 ? 3 : 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr bool DK = PART == 2;
   constexpr int KS = D / 32, CT = D / 32;
   constexpr int QH = 64;                                   // queries per half tile
@@ -524,18 +525,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
       // masked entries take s = -inf, so P = 0 (and dS = 0)
       const int base_it = 32 * sub + 4 * hh;
       const int lo = (a.causal ? kj - q0 : 0) - base_it, hi = (k_ok ? a.N - 1 - q0 : -1) - base_it;
-      float4 qs4[4], l4[4];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        qs4[a4] = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
-        l4[a4] = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
-      }
       float x[16], p[16];
+      if constexpr (DK) {
+        float4 qs4[4], l4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float qs = reinterpret_cast<const float*>(&qs4[r >> 2])[r & 3];
-        const float lr = reinterpret_cast<const float*>(&l4[r >> 2])[r & 3];
-        x[r] = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
+        for (int a4 = 0; a4 < 4; ++a4) {
+          qs4[a4] = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
+          l4[a4] = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float qs = reinterpret_cast<const float*>(&qs4[r >> 2])[r & 3];
+          const float lr = reinterpret_cast<const float*>(&l4[r >> 2])[r & 3];
+          x[r] = static_cast<float>(S[r]) * (qs * dk_j) + bj - lr;
+        }
+      } else {
+        // each quad of per-query scalars loaded where it is used: fewer live
+        // registers, so that three dV work-groups fit on a CU
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float4 qs4 = *reinterpret_cast<const float4*>(tqs + base_it + 8 * a4);
+          const float4 l4 = *reinterpret_cast<const float4*>(tl + base_it + 8 * a4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            x[4 * a4 + u] = static_cast<float>(S[4 * a4 + u]) * (reinterpret_cast<const float*>(&qs4)[u] * dk_j) + bj -
+                            reinterpret_cast<const float*>(&l4)[u];
+        }
       }
       if (!full)   // uniform
 #pragma unroll
