@@ -80,6 +80,32 @@ def test_layout_sizes(gran, gq, gk):
     assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
 
 
+def test_bwd_layout_sizes():
+    """Every span of the backward workspace has the size include/sage.h states,
+    is 256-byte aligned and overlaps no other."""
+    B, H, N, d = 2, 3, 1000, 128
+    n_pad, nblk, BH = 1024, 8, 6
+    lay = L.BwdLayout()
+    assert L.lib().sage_bwd_workspace_layout(ctypes.byref(_shape(B, H, N, d)), ctypes.byref(_params()),
+                                             ctypes.byref(lay)) == L.SAGE_OK
+    assert lay.n_pad == n_pad
+    row = BH * n_pad * 4
+    expect = {"do_codes": BH * n_pad * d, "do_scale": row, "do_mean": BH * nblk * d * 4,
+              "v_codes": BH * n_pad * d, "v_scale": BH * (n_pad // 16) * 4, "v_mean": BH * d * 4,
+              "v_partial": BH * nblk * d * 4, "fp8_partial": BH * nblk * 3 * d * 4,
+              "dsum": row, "lse_do": row, "dsum_do": row}
+    for n in ("do8", "q8", "k8"):
+        expect.update({f"{n}_codes": BH * d * n_pad, f"{n}_scale": BH * d * 4, f"{n}_mean": BH * d * 4})
+    assert set(expect) == set(L.BWD_SPANS)
+    spans = sorted((getattr(lay, n).offset, getattr(lay, n).bytes, n) for n in L.BWD_SPANS)
+    for (off, size, name) in spans:
+        assert size == expect[name], name
+        assert off % 256 == 0
+    for (a, b) in zip(spans, spans[1:]):
+        assert a[0] + a[1] <= b[0]
+    assert spans[-1][0] + spans[-1][1] <= lay.total_bytes
+
+
 @pytest.mark.parametrize("mode", ["mxfp4", "pv16", "int_e4m3", "int_e2m3"])
 def test_layout_sizes_other_formats(mode):
     """MXFP4 codes are 4 bits (d/2 bytes per token) with one scale byte per 32
