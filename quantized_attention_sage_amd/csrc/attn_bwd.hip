@@ -23,9 +23,11 @@
 //    block; lane l holds key l%32.  S = Q^ K^T (and dP = dO^ V^T) put a key's
 //    16 queries of each 32-query subtile in one lane, for dV^T += dO^T P and
 //    dK^T += Q^T dS.  Split in two so that each holds one accumulator set and
-//    two work-groups fit on a CU (the dK kernel recomputes S and P).
+//    two work-groups fit on a CU (dV: three; the dK kernel recomputes S and P).
 // Each walks the other axis in 64-row half tiles through a three-slot LDS
-// ring filled by direct global-to-LDS copies two half tiles ahead.
+// ring filled by direct global-to-LDS copies two half tiles ahead; work-group
+// ids are regrouped so that each XCD runs a contiguous run of (head, block)
+// items, whose streamed rows are then fetched into that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
