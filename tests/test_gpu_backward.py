@@ -164,13 +164,16 @@ def test_backward_parity(case):
     for nm, gg, ee, xx in zip(("dQ", "dK", "dV"), r["grads"], em, ex):
         err = np.abs(gg - ee)
         scale = np.abs(ee).max()
-        m_g, m_e = oracle.compare(xx, gg), oracle.compare(xx, ee)
+        # N = 1: dQ = dK = 0 exactly, and the metrics against exact gradients are undefined
+        defined = np.abs(xx).max() > 1e-12
+        m_g, m_e = (oracle.compare(xx, gg), oracle.compare(xx, ee)) if defined else ({}, {})
+        vs_exact = (f"vs exact gpu cos {m_g['cos']:.6f} relL1 {m_g['rel_l1']:.4f}, emul cos {m_e['cos']:.6f} "
+                    f"relL1 {m_e['rel_l1']:.4f}") if defined else "exact gradient is zero"
         log(f"  {nm}: max|gpu - emul| = {err.max():.3e} ({err.max() / max(scale, 1e-30):.2e} of max|G|), "
-            f"rel L1 {err.sum() / max(np.abs(ee).sum(), 1e-30):.2e}; vs exact gpu cos {m_g['cos']:.6f} "
-            f"relL1 {m_g['rel_l1']:.4f}, emul cos {m_e['cos']:.6f} relL1 {m_e['rel_l1']:.4f}")
+            f"rel L1 {err.sum() / max(np.abs(ee).sum(), 1e-30):.2e}; {vs_exact}")
         assert err.sum() <= 5e-4 * np.abs(ee).sum() + 1e-30, f"{nm}: sum |G - E| / sum |E| too large"
         assert np.all(err <= 1e-2 * scale + 1e-30), f"{nm}: {int((err > 1e-2 * scale).sum())} elements beyond 1e-2 max|E|"
-        if np.abs(xx).max() > 1e-12:     # N = 1: dQ = dK = 0 exactly and the metrics are undefined
+        if defined:
             assert abs(m_g["cos"] - m_e["cos"]) <= 1e-4 and abs(m_g["rel_l1"] - m_e["rel_l1"]) <= 5e-4
 
 
