@@ -101,6 +101,25 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+NOMINAL_GHZ = 2.4   # the clock the published matrix peaks are quoted at
+N_XCD = 8
+
+
+def cycles_from_profile(workload: str):
+    """GPU cycles per attention launch on one XCD (GRBM_GUI_ACTIVE summed over
+    the 8 XCDs, divided by 8) from the committed rocprofv3 counter summary, or
+    None when it is missing or the kernel changed since."""
+    try:
+        with open(COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    g = rec.get("grbm_gui_active_per_dispatch")
+    return None if g is None else g / N_XCD
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -413,6 +432,16 @@ def main():
     traffic = None if (pv16 or mx or args.qk != "int") else traffic_from_profile(w.name)
     qtraffic = None if (pv16 or mx or args.qk != "int") else quant_traffic_from_profile(w.name)
     qk_bytes, v_bytes = quant_bytes(w, args.pv, args.qk)
+    # The clock the kernel sustains: its cycles per launch (a count of work,
+    # much the same on every box) over this run's launch time.
+    cycles = None if (pv16 or mx or args.qk != "int") else cycles_from_profile(w.name)
+    clock = None
+    if cycles is not None:
+        ghz = cycles / (attn_ms * 1e-3) / 1e9
+        clock = {"ghz": round(ghz, 3), "cycles_per_launch": round(cycles),
+                 "frac_at_clock": round(attn_tops / (peak * ghz / NOMINAL_GHZ), 4),
+                 "source": "GRBM_GUI_ACTIVE per XCD per launch (profiles/attn_fwd_counters.json) "
+                           "over this run's launch time"}
     rec = {
         "metric": "attention TOPS (4*B*H*N^2*d, halved if causal) of quant_qk + quant_v + attn_fwd",
         "value": round(tops, 2),
@@ -436,7 +465,7 @@ def main():
                      "frac": round(attn_tops / peak, 4), "traffic": traffic,
                      "kernel": "attn_pvh_kernel" if pv16 else ("attn_fp4_kernel" if mx else "attn_fwd_kernel"),
                      "kernel_ms": round(attn_ms, 4),
-                     "ops_per_launch": w.ops},
+                     "ops_per_launch": w.ops, "sustained_clock": clock},
         "breakdown_ms": {"quant_qk": round(qk_ms, 4), "quant_v": round(v_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "quant_roofline": {
             "bound": "hbm", "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -86,6 +86,24 @@ def test_counter_records_follow_the_sources(tmp_path, monkeypatch):
     assert bench.quant_traffic_from_profile(r["workload"]) is None
 
 
+def test_clock_record_is_consistent(tmp_path, monkeypatch):
+    r = _load("attn_fwd_counters.json")
+    # GRBM_GUI_ACTIVE is summed over the 8 XCDs; its per-XCD count over the
+    # dispatch time under counters is the clock in that run
+    assert r["clock_ghz_under_counters"] == pytest.approx(r["grbm_gui_active_per_dispatch"] / 8
+                                                          / (r["dispatch_us_under_counters"] * 1e3))
+    assert 1.0 < r["clock_ghz_under_counters"] <= 2.4
+    got = bench.cycles_from_profile(r["workload"])
+    if r["kernel_source_hash"] == bench.kernel_source_hash():
+        assert got == pytest.approx(r["grbm_gui_active_per_dispatch"] / 8)
+    else:
+        assert got is None
+    p = tmp_path / "a.json"
+    p.write_text(json.dumps(dict(r, kernel_source_hash="0" * 16)))
+    monkeypatch.setattr(bench, "COUNTERS", str(p))
+    assert bench.cycles_from_profile(r["workload"]) is None
+
+
 def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
