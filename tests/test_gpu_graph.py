@@ -64,3 +64,73 @@ def test_graph_replay_matches_eager(qk_format, pv):
     torch.cuda.synchronize()
     assert torch.equal(replayed, out)
     assert not torch.equal(replayed, ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_training_step_graph_replay_matches_eager(causal):
+    """The 8-bit training step (both quantisation calls, the forward with L and
+    the backward, whose operand passes reuse the quantisation kernels) captured
+    once: every replay equals the eager O, L and gradients bit for bit, and a
+    replay after dO changes in place equals the eager step on the new dO."""
+    import torch
+    from quantized_attention_sage_amd import api
+    from quantized_attention_sage_amd.workloads import make_grad
+
+    w = scaled(WORKLOADS["target_causal" if causal else "target"], H=2, N=700)
+    log(f"training-step graph case: H={w.H} N={w.N} causal={causal}")
+    q, k, v = make_inputs(w)
+    qt, kt, vt = (to_device(x, w.dtype) for x in (q, k, v))
+    params = api.make_params(qk_bits=8, gran="thread")   # the backward's setting
+    shape = api.make_shape(qt, kt, vt)
+    ws = api.Workspace(shape, params, qt.device)
+    bws = api.BwdWorkspace(shape, params, qt.device)
+    out = torch.empty_like(qt)
+    do = to_device(make_grad(w), w.dtype)
+    lse = torch.empty((w.B, w.H, ws.layout.n_pad), dtype=torch.float32, device=qt.device)
+    grads = [torch.empty(qt.shape, dtype=torch.float32, device=qt.device) for _ in range(3)]
+
+    def step():
+        api.quant_qk(qt, kt, vt, params, ws, shape)
+        api.quant_v(vt, params, ws, shape)
+        api.attn_fwd_lse(ws, shape, params, causal, out, lse)
+        api.attn_bwd(qt, kt, vt, out, do, lse, ws, shape, params, causal, bws, *grads)
+
+    def results():
+        return [out.clone(), lse.clone()] + [g_.clone() for g_ in grads]
+
+    def clear():
+        for t_ in [out, lse, ws.tensor, bws.tensor] + grads:
+            t_.zero_()
+
+    step()
+    torch.cuda.synchronize()
+    ref = results()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    names = ("O", "L", "dQ", "dK", "dV")
+    for r in range(3):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, a, b in zip(names, results(), ref):
+            assert torch.equal(a, b), f"replay {r}: {n} differs from the eager step"
+
+    do.mul_(2)                       # exact: the replay must read the new dO
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = results()
+    step()
+    torch.cuda.synchronize()
+    for n, a, b in zip(names, replayed, results()):
+        assert torch.equal(a, b), f"{n}: the replay after dO changed differs from the eager step"
+    assert not torch.equal(replayed[4], ref[4])
