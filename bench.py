@@ -414,6 +414,7 @@ def main():
     qk_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     v_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    attn_ms_median = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
 
     if args.calibrate_copy:
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -464,7 +465,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(attn_tops / peak, 4), "traffic": traffic,
                      "kernel": "attn_pvh_kernel" if pv16 else ("attn_fp4_kernel" if mx else "attn_fwd_kernel"),
-                     "kernel_ms": round(attn_ms, 4),
+                     "kernel_ms": round(attn_ms, 4), "kernel_ms_median": round(attn_ms_median, 4),
                      "ops_per_launch": w.ops, "sustained_clock": clock},
         "breakdown_ms": {"quant_qk": round(qk_ms, 4), "quant_v": round(v_ms, 4), "attn_fwd": round(attn_ms, 4)},
         "quant_roofline": {
